@@ -1,0 +1,156 @@
+"""The fp64 oracle against its pins (CPU only).
+
+* Every pin in ``oracle_pins`` runs against the C oracle and the numpy oracle.
+* The two oracles agree to 1e-12 on random inputs and the tiny workload.
+* Mistakes planted in copies of the numpy oracle (swapped order, read before
+  write, gate on the wrong axis, dropped beta, sign and transpose errors, ...)
+  each fail at least one pin, which shows the pins can tell a wrong recurrence
+  from the right one.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import kda_inputs
+import oracle
+from oracle.ref_numpy import kda_fwd_numpy
+
+from oracle_pins import ALL_PINS
+
+
+def c_fwd(q, k, v, g, beta, h0, scale):
+    return oracle.kda_fwd(q, k, v, g, beta, h0=h0, scale=scale)
+
+
+def np_fwd(q, k, v, g, beta, h0, scale):
+    return kda_fwd_numpy(q, k, v, g, beta, h0=h0, scale=scale)
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+@pytest.mark.parametrize("impl", [c_fwd, np_fwd], ids=["c", "numpy"])
+def test_pin(pin, impl):
+    pin(impl)
+
+
+def test_two_oracles_agree_random():
+    rng = np.random.default_rng(123)
+    B, T, H, Dk, Dv = 2, 40, 3, 16, 12
+    q = rng.standard_normal((B, T, H, Dk))
+    k = rng.standard_normal((B, T, H, Dk)) / 4
+    v = rng.standard_normal((B, T, H, Dv))
+    g = -5 / (1 + np.exp(-rng.standard_normal((B, T, H, Dk))))
+    beta = rng.uniform(0, 1, (B, T, H))
+    h0 = rng.standard_normal((B, H, Dk, Dv))
+    o1, S1 = oracle.kda_fwd(q, k, v, g, beta, h0=h0)
+    o2, S2 = kda_fwd_numpy(q, k, v, g, beta, h0=h0)
+    assert np.abs(o1 - o2).max() <= 1e-12 * np.abs(o2).max()
+    assert np.abs(S1 - S2).max() <= 1e-12 * np.abs(S2).max()
+
+
+def test_two_oracles_agree_tiny_workload():
+    x = kda_inputs.config_inputs(kda_inputs.TINY)
+    args = [x[n].double().numpy() for n in ("q", "k", "v", "g", "beta")]
+    o1, S1 = oracle.kda_fwd(*args, h0=None)
+    o2, S2 = kda_fwd_numpy(*args, h0=None)
+    assert np.abs(o1 - o2).max() <= 1e-12 * np.abs(o2).max()
+    assert np.abs(S1 - S2).max() <= 1e-12 * np.abs(S2).max()
+
+
+def test_decode_is_one_token_prefill():
+    x = kda_inputs.decode_inputs(3, 2, 8, "f32", seed=5)
+    args = [x[n].double().numpy() for n in ("q", "k", "v", "g", "beta")]
+    o, S = oracle.kda_decode(*args, x["state"].double().numpy())
+    o2, S2 = kda_fwd_numpy(*[a[:, None] for a in args], h0=x["state"].double().numpy())
+    assert np.abs(o - o2[:, 0]).max() < 1e-13
+    assert np.abs(S - S2).max() < 1e-13
+
+
+def test_oracle_rejects_bad_dims():
+    with pytest.raises(AssertionError):
+        oracle.kda_fwd(np.zeros((1, 2, 1, 4)), np.zeros((1, 2, 1, 3)), np.zeros((1, 2, 1, 4)),
+                       np.zeros((1, 2, 1, 4)), np.zeros((1, 2, 1)))
+
+
+def test_oracle_empty_sequence_returns_h0():
+    h0 = np.arange(12.0).reshape(1, 1, 3, 4)
+    z = np.zeros((1, 0, 1, 3))
+    o, S = oracle.kda_fwd(z, z, np.zeros((1, 0, 1, 4)), z, np.zeros((1, 0, 1)), h0=h0)
+    assert o.shape == (1, 0, 1, 4)
+    assert np.array_equal(S, h0)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each mutant is the numpy oracle with one plausible error.
+# ---------------------------------------------------------------------------
+
+def _mutant(kind):
+    def fwd(q, k, v, g, beta, h0, scale):
+        q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))
+        B, T, H, Dk = q.shape
+        Dv = v.shape[-1]
+        S = np.zeros((B, H, Dk, Dv)) if h0 is None else np.array(h0, dtype=np.float64)
+        o = np.zeros((B, T, H, Dv))
+        for t in range(T):
+            a = np.exp(g[:, t])
+            if kind == "erase_before_decay":
+                r = np.einsum("bhij,bhi->bhj", S, k[:, t])
+                S = a[..., None] * S
+            else:
+                if kind == "decay_value_axis":
+                    S = S * a[..., None, :]
+                elif kind == "no_decay":
+                    pass
+                elif kind == "decay_sign":
+                    S = np.exp(-g[:, t])[..., None] * S
+                else:
+                    S = a[..., None] * S
+                if kind == "recall_transposed":
+                    r = np.einsum("bhji,bhi->bhj", S, k[:, t])
+                else:
+                    r = np.einsum("bhij,bhi->bhj", S, k[:, t])
+            o_before = scale * np.einsum("bhij,bhi->bhj", S, q[:, t])
+            if kind == "no_beta":
+                e = v[:, t] - r
+            elif kind == "erase_sign":
+                e = beta[:, t][..., None] * (v[:, t] + r)
+            elif kind == "beta_on_value_only":
+                e = beta[:, t][..., None] * v[:, t] - r
+            elif kind == "no_erase":
+                e = beta[:, t][..., None] * v[:, t]
+            else:
+                e = beta[:, t][..., None] * (v[:, t] - r)
+            S = S + k[:, t][..., :, None] * e[..., None, :]
+            if kind == "read_before_write":
+                o[:, t] = o_before
+            elif kind == "read_transposed":
+                o[:, t] = scale * np.einsum("bhji,bhi->bhj", S, q[:, t])
+            elif kind == "no_scale":
+                o[:, t] = np.einsum("bhij,bhi->bhj", S, q[:, t])
+            else:
+                o[:, t] = scale * np.einsum("bhij,bhi->bhj", S, q[:, t])
+        return o, S
+    return fwd
+
+
+MUTANTS = ["erase_before_decay", "decay_value_axis", "no_decay", "decay_sign", "recall_transposed",
+           "no_beta", "erase_sign", "beta_on_value_only", "no_erase", "read_before_write",
+           "read_transposed", "no_scale"]
+
+
+def test_unmutated_copy_passes_all_pins():
+    fwd = _mutant("none")
+    for pin in ALL_PINS:
+        pin(fwd)
+
+
+@pytest.mark.parametrize("kind", MUTANTS)
+def test_planted_mistake_is_caught(kind):
+    fwd = _mutant(kind)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(fwd)
+        except Exception:  # AssertionError or a shape error from the broken code
+            failed.append(pin.__name__)
+    assert failed, "mutant %s passed every pin" % kind
