@@ -1,0 +1,217 @@
+"""Benchmark of the KDA forward hot path on one MI355X.
+
+One step = one chunked prefill over the 64K-token full-width workload
+(B=1, H=56, T=65536, d=128, bf16 q/k/v, fp32 g/beta/o/state) followed by one
+decode step over 256 sequences x 56 heads (fp32 state updated in place).
+Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout:
+  value          prefill tokens/s (B*T / mean prefill kernel time)
+  roofline       the prefill kernel against the HBM roofline (algorithmic bytes)
+  decode         the decode kernel's algorithmic GB/s against the HBM peak
+  cpu_baseline   the fp64 oracle on the host cores, on a bounded token sample
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (H=56,d=128,T=64K); decode-step HBM GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_prefill_64k_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_recurrence_10_amd", "csrc", f)
+                  for f in ("kda_prefill_valu.hip", "kda_prefill_mfma.hip", "kda_api.cpp")]
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def prefill_bytes(B, T, H, D, in_bytes=2, h0=False, hT=True):
+    """Algorithmic HBM bytes of one prefill: q, k, v (in dtype), g (fp32) and
+    beta (fp32) read once, o (fp32) written once, states read/written once."""
+    per_tok_head = 3 * D * in_bytes + 4 * D + 4 + 4 * D
+    state = 4 * D * D
+    return B * T * H * per_tok_head + B * H * state * (int(h0) + int(hT))
+
+
+def decode_bytes(B, H, D, in_bytes=2):
+    """State read + written once, q, k, v in dtype, g fp32, beta fp32, o fp32."""
+    return B * H * (2 * 4 * D * D + 3 * D * in_bytes + 4 * D + 4 + 4 * D)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per prefill launch from committed rocprofv3 counter runs, or
+    None when they are missing or were taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_src_sha") != source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(target_s: float):
+    """Time the fp64 oracle on a prefix of the same workload (all 56 heads)."""
+    import numpy as np
+    import kda_inputs
+    import oracle
+
+    cfg = kda_inputs.PREFILL_64K
+    threads = oracle.num_threads()
+
+    def run(T):
+        x = kda_inputs.prefill_inputs(cfg.B, T, cfg.H, cfg.D, cfg.dtype, seed=cfg.seed, device="cpu")
+        args = [np.ascontiguousarray(x[n].double().numpy()) for n in ("q", "k", "v", "g", "beta")]
+        t0 = time.perf_counter()
+        oracle.kda_fwd(*args)
+        return time.perf_counter() - t0
+
+    probe_T = 64
+    dt = run(probe_T)
+    T = int(min(cfg.T, max(probe_T, probe_T * target_s / max(dt, 1e-6))))
+    T = max(16, T // 16 * 16)
+    dt = run(T)
+    return {
+        "value": cfg.B * T / dt,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "first %d of %d tokens of the B=1 H=56 d=128 workload, all heads, fp64 token-sequential C "
+                  "(OpenMP over heads), %.1f s wall" % (T, cfg.T, dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the KDA forward path here runs on a single MI355X and has no "
+              "multi-GPU mode (asked for --gpus %d, WORLD_SIZE=%d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kda_inputs
+    import linear_attention_recurrence_10_amd as kda
+
+    if not os.path.exists(kda.library_path()):
+        log("libkda.so missing: building")
+        from linear_attention_recurrence_10_amd import build
+        build.build()
+    kda.library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg = kda_inputs.PREFILL_64K
+    log("generating %s on the device" % cfg.name)
+    x = kda_inputs.config_inputs(cfg, device=dev)
+    o = torch.empty((cfg.B, cfg.T, cfg.H, cfg.D), dtype=torch.float32, device=dev)
+    hT = torch.empty((cfg.B, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dev)
+    dcfg = kda_inputs.DECODE_B256
+    d = None
+    if not args.no_decode:
+        d = kda_inputs.decode_inputs(dcfg.B, dcfg.H, dcfg.D, dcfg.dtype, seed=dcfg.seed, device=dev)
+        od = torch.empty((dcfg.B, dcfg.H, dcfg.D), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], None, o=o, hT=hT, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        if d is not None:
+            kda.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], o=od, stream=stream)
+            if ev:
+                ev[2].record(stream)
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [e[0].elapsed_time(e[1]) for e in events]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in events] if d is not None else []
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    ms_per_step = 1e3 * wall / args.steps
+    log("prefill avg %.3f ms (min %.3f), decode avg %s ms, wall/step %.3f ms" % (
+        pre_avg, min(pre_ms), ("%.3f" % (sum(dec_ms) / len(dec_ms))) if dec_ms else "-", ms_per_step))
+
+    tokens = cfg.B * cfg.T
+    pbytes = prefill_bytes(cfg.B, cfg.T, cfg.H, cfg.D, 2, h0=False, hT=True)
+    achieved = pbytes / (pre_avg * 1e-3) / 1e9
+    traffic = load_traffic()
+    result = {
+        "metric": METRIC,
+        "value": tokens / (pre_avg * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "T": cfg.T, "d_k": cfg.D, "d_v": cfg.D,
+                   "chunk": kda_inputs.CHUNK, "inputs": "q,k,v bf16; g,beta fp32; o,state fp32",
+                   "decode_workload": None if d is None else dcfg.name},
+        "prefill_ms": pre_avg,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "kda prefill", "alg_bytes_per_launch": pbytes},
+    }
+    if d is not None:
+        dbytes = decode_bytes(dcfg.B, dcfg.H, dcfg.D, 2)
+        dec_avg = sum(dec_ms) / len(dec_ms)
+        dg = dbytes / (dec_avg * 1e-3) / 1e9
+        result["decode"] = {"workload": dcfg.name, "ms": dec_avg, "achieved": dg, "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": dg / HBM_PEAK_GBPS, "alg_bytes_per_launch": dbytes}
+    if not args.no_cpu_baseline:
+        del x, o, hT
+        log("cpu baseline (oracle), ~%.0f s" % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,121 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ *
+ * The operation (per batch row b and head h; one state per head):
+ *
+ *   S <- h0                                     d_k x d_v, fp32
+ *   for each token t:
+ *     S <- Diag(exp(g_t)) S                     decay every key channel first
+ *     S <- S + beta_t k_t (v_t - S^T k_t)^T     recall with the incoming key,
+ *                                               then write only the difference
+ *     o_t = scale * S^T q_t                     read after the write
+ *   hT <- S
+ *
+ * Sources: "Kimi K3 Architecture Explained: How the World's Largest Open
+ * Source AI Model Works", section 3 "Kimi Delta Attention (KDA)" (the
+ * decay -> erase -> write order and DeltaNet's difference write); the Kimi K3
+ * paper digest on devpress.csdn.net, section 2.1 (1) (delta-rule recursion
+ * with a per-channel forget gate on a fixed-size state; gate bounded below by
+ * g_min = -5 with 16-token chunks so that in-chunk reciprocal factors stay in
+ * bf16 range) and section 2.4 (1) (the FlashKDA kernel overlaps intra-chunk
+ * parallel work with inter-chunk state propagation).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers on the calling thread's current
+ *    HIP device, owned by the caller.  The library allocates no device
+ *    memory and keeps no state between calls besides cached device
+ *    properties.  Calls are thread-safe.
+ *  - Every call is asynchronous and ordered on `stream` (a hipStream_t passed
+ *    as void*; NULL = the null stream).  The library never synchronises.
+ *  - Layouts are dense, row-major, token-major:
+ *        q, k, g  [B, T, H, Dk]      v, o  [B, T, H, Dv]      beta [B, T, H]
+ *        states   [B, H, Dk, Dv]     (row index = key channel)
+ *    q, k, v are stored in `in_dtype`; g, beta, states and o are fp32.
+ *  - g is the log-decay, expected in [-5, 0] (the bounded gate above); values
+ *    outside are not clamped, but g < -5 may underflow the in-chunk factors.
+ *  - scale <= 0 selects Dk^-1/2.
+ *  - Supported shapes: Dk == Dv in {16, 128}.  Indices are 64-bit, so any B*T*H
+ *    that fits in device memory is accepted.
+ *  - Argument errors are detected before anything is launched and return
+ *    KDA_ERR_INVALID_ARGUMENT or KDA_ERR_UNSUPPORTED; kda_last_error() then
+ *    describes the problem.  A failed launch returns KDA_ERR_LAUNCH.  No C++
+ *    exception crosses this interface.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misalignment, overlap */
+    KDA_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement */
+    KDA_ERR_LAUNCH = 3,           /* the HIP runtime rejected a launch */
+    KDA_ERR_DEVICE = 4            /* no usable device / unsupported architecture */
+} kda_status;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0,
+    KDA_BF16 = 1
+} kda_dtype;
+
+/*
+ * kda_chunk_fwd -- chunked prefill over a whole sequence, with an optional
+ * initial state (prefix reuse: the digest's section 2.4 (4) keeps sparse KDA
+ * state checkpoints so that cached prefixes can be resumed).
+ *
+ *   q, k   [B, T, H, Dk]  in_dtype   queries and keys (any norm; callers
+ *                                    usually L2-normalise them)
+ *   v      [B, T, H, Dv]  in_dtype   values
+ *   g      [B, T, H, Dk]  fp32       per-channel log-decay
+ *   beta   [B, T, H]      fp32       write strength
+ *   h0     [B, H, Dk, Dv] fp32       initial state, or NULL for zeros
+ *   o      [B, T, H, Dv]  fp32       output, written (must not overlap any input)
+ *   hT     [B, H, Dk, Dv] fp32       final state, written; NULL = not wanted.
+ *                                    hT == h0 (exact alias) is allowed: the
+ *                                    state is then updated in place.
+ *
+ * T need not be a multiple of the 16-token chunk; T == 0 copies h0 (or zeros)
+ * to hT.  B, H, Dk, Dv must be positive; T >= 0.  All pointers 16-byte aligned.
+ */
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, const float *h0,
+                         float *o, float *hT,
+                         int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                         kda_dtype in_dtype, float scale, void *stream);
+
+/*
+ * kda_decode_step -- one new token per sequence (recurrent decoding, the case
+ * behind the 4x decoding speed-up at 1M tokens quoted in "Kimi K3
+ * Architecture Explained", section 3): the recurrence above with T = 1,
+ * updating the state IN PLACE.
+ *
+ *   q, k   [B, H, Dk]  in_dtype     v [B, H, Dv] in_dtype
+ *   g      [B, H, Dk]  fp32         beta [B, H] fp32
+ *   state  [B, H, Dk, Dv] fp32      read, then overwritten with the new state
+ *   o      [B, H, Dv]  fp32         written (must not overlap anything else)
+ */
+kda_status kda_decode_step(const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           float *state, float *o,
+                           int64_t B, int64_t H, int64_t Dk, int64_t Dv,
+                           kda_dtype in_dtype, float scale, void *stream);
+
+/* Human-readable name of a status code (static string). */
+const char *kda_status_string(kda_status s);
+
+/* Description of the last error returned on the calling thread ("" if none). */
+const char *kda_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,165 @@
+"""Python binding of the MI355X KDA forward library (``libkda.so``, include/kda.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch provides device memory and the current
+stream.  If the library has not been built this module raises on first use;
+there is no CPU fallback.
+
+    o, hT = chunk_fwd(q, k, v, g, beta, h0)      # prefill, optional initial state
+    o = decode_step(q, k, v, g, beta, state)     # one token, state updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = ["chunk_fwd", "decode_step", "KdaError", "library", "library_path", "version"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkda.so")
+_lock = threading.Lock()
+_lib = None
+
+KDA_OK = 0
+KDA_F32 = 0
+KDA_BF16 = 1
+
+
+class KdaError(RuntimeError):
+    """A non-OK status from the C ABI; ``status`` holds the code."""
+
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__("%s: %s" % (name, detail))
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library() -> ctypes.CDLL:
+    """The loaded ``libkda.so`` with argument types set (raises if not built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError("libkda.so is not built (run `python -m linear_attention_recurrence_10_amd.build`)")
+            lib = ctypes.CDLL(_LIB_PATH)
+            vp, fp, i64 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64
+            lib.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, i64, i64, i64, i64, i64,
+                                          ctypes.c_int, ctypes.c_float, vp]
+            lib.kda_chunk_fwd.restype = ctypes.c_int
+            lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, i64, i64, i64, i64,
+                                            ctypes.c_int, ctypes.c_float, vp]
+            lib.kda_decode_step.restype = ctypes.c_int
+            lib.kda_status_string.argtypes = [ctypes.c_int]
+            lib.kda_status_string.restype = ctypes.c_char_p
+            lib.kda_last_error.argtypes = []
+            lib.kda_last_error.restype = ctypes.c_char_p
+            lib.kda_version.argtypes = []
+            lib.kda_version.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def version() -> int:
+    return int(library().kda_version())
+
+
+def _check(status: int) -> None:
+    if status != KDA_OK:
+        lib = library()
+        raise KdaError(status, lib.kda_status_string(status).decode(), lib.kda_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def chunk_fwd(q, k, v, g, beta, h0=None, *, scale: float | None = None, o=None, hT=None,
+              output_final_state: bool = True, stream=None):
+    """Chunked KDA prefill (``kda_chunk_fwd``).
+
+    q, k: [B, T, H, Dk] and v: [B, T, H, Dv] (bf16 or fp32, same dtype); g:
+    [B, T, H, Dk] fp32; beta: [B, T, H] fp32; h0: [B, H, Dk, Dv] fp32 or None.
+    Returns (o [B, T, H, Dv] fp32, hT [B, H, Dk, Dv] fp32 or None).  ``o`` and
+    ``hT`` may be given to write into (``hT`` may be ``h0`` itself).
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.float32)
+    if hT is None and output_final_state:
+        hT = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if hT is not None:
+        _need(hT, "hT", torch.float32)
+    shapes_ok = (k.shape == q.shape and g.shape == q.shape and v.shape[:3] == (B, T, H)
+                 and beta.shape == (B, T, H) and o.shape == (B, T, H, Dv)
+                 and (h0 is None or h0.shape == (B, H, Dk, Dv))
+                 and (hT is None or hT.shape == (B, H, Dk, Dv)))
+    if not shapes_ok:
+        raise ValueError("inconsistent shapes")
+    lib = library()
+    _check(lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
+                             B, T, H, Dk, Dv, _dtype_code(q), float(scale or 0.0), _stream(stream)))
+    return o, hT
+
+
+def decode_step(q, k, v, g, beta, state, *, scale: float | None = None, o=None, stream=None):
+    """One-token KDA update (``kda_decode_step``); ``state`` is updated in place.
+
+    q, k: [B, H, Dk], v: [B, H, Dv] (bf16 or fp32); g: [B, H, Dk] fp32; beta:
+    [B, H] fp32; state: [B, H, Dk, Dv] fp32.  Returns o [B, H, Dv] fp32.
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32)
+    _need(state, "state", torch.float32)
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, H, Dv), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.float32)
+    if not (k.shape == q.shape and g.shape == q.shape and v.shape[:2] == (B, H) and beta.shape == (B, H)
+            and state.shape == (B, H, Dk, Dv) and o.shape == (B, H, Dv)):
+        raise ValueError("inconsistent shapes")
+    lib = library()
+    _check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+                               B, H, Dk, Dv, _dtype_code(q), float(scale or 0.0), _stream(stream)))
+    return o

@@ -1,0 +1,78 @@
+"""Build ``libkda.so`` (the C-ABI library of include/kda.h) for gfx950 with hipcc.
+
+Run as ``python -m linear_attention_recurrence_10_amd.build``; the repository's
+``__graft_entry__.build()`` calls :func:`build` as well.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libkda.so")
+SOURCES = ["kda_api.cpp", "kda_prefill_valu.hip", "kda_prefill_mfma.hip", "kda_decode.hip"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    # no packed fp32 instructions (v_pk_fma_f32 and friends) in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compile every source to an object in a temp dir, link libkda.so in place."""
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    with tempfile.TemporaryDirectory(prefix="kda_build_") as tmp:
+        procs = []
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            lang = ["-x", "hip"] if src.endswith(".hip") else []
+            cmd = [hipcc()] + HIPCC_FLAGS + inc + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+            objs.append(obj)
+            if len(procs) >= jobs:
+                _drain(procs[:1])
+                procs = procs[1:]
+        _drain(procs)
+        tmp_lib = os.path.join(tmp, "libkda.so")
+        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_lib] + objs
+        subprocess.run(cmd, check=True)
+        shutil.copyfile(tmp_lib, LIB + ".tmp")
+        os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+def _drain(procs):
+    for src, p in procs:
+        out, _ = p.communicate()
+        text = out.decode(errors="replace")
+        # hipcc's host pass does not know the device-only feature flag; that warning is harmless
+        lines = [l for l in text.splitlines() if "packed-fp32-ops" not in l and l.strip()]
+        if p.returncode != 0:
+            sys.stderr.write(text)
+            raise RuntimeError("hipcc failed on %s" % src)
+        if lines:
+            sys.stderr.write("\n".join(lines) + "\n")
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,228 @@
+// kda_api.cpp -- the C ABI declared in include/kda.h: argument validation,
+// kernel selection and launch on the caller's stream.
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kda_status fail(kda_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+kda_status ok() {
+    g_last_error[0] = '\0';
+    return KDA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+    const char *name;
+    const void *p;
+    uint64_t bytes;
+};
+
+bool overlaps(const Span &a, const Span &b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Product of positive sizes with an overflow check (false on overflow).
+bool mul_ok(uint64_t &acc, int64_t x) {
+    if (x < 0) return false;
+    if (x != 0 && acc > UINT64_MAX / static_cast<uint64_t>(x)) return false;
+    acc *= static_cast<uint64_t>(x);
+    return true;
+}
+
+// Architecture check, cached per device ordinal: 0 unknown, 1 gfx950, 2 other.
+std::atomic<int> g_arch[64];
+
+kda_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return fail(KDA_ERR_DEVICE, "no current HIP device");
+    if (dev < 64) {
+        int st = g_arch[dev].load(std::memory_order_relaxed);
+        if (st == 1) return KDA_OK;
+        if (st == 2) return fail(KDA_ERR_DEVICE, "device %d is not gfx950", dev);
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return fail(KDA_ERR_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+    const bool good = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_arch[dev].store(good ? 1 : 2, std::memory_order_relaxed);
+    if (!good) return fail(KDA_ERR_DEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
+    return KDA_OK;
+}
+
+// A tensor argument must be a device allocation that covers all of its bytes,
+// so that a wrong pointer or size is rejected here instead of faulting the GPU.
+kda_status check_device_span(const Span &s) {
+    if (!s.p || s.bytes == 0) return KDA_OK;
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void *>(s.p)) != hipSuccess || base == nullptr) {
+        (void)hipGetLastError();
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not a device allocation", s.name);
+    }
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(base), p0 = reinterpret_cast<uintptr_t>(s.p);
+    if (p0 + s.bytes > b0 + size)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: %llu bytes from the pointer run past the end of its allocation",
+                    s.name, static_cast<unsigned long long>(s.bytes));
+    return KDA_OK;
+}
+
+kda_status check_spans(const Span *sp, int n) {
+    for (int i = 0; i < n; ++i) {
+        if (sp[i].p && !aligned16(sp[i].p))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", sp[i].name);
+    }
+    for (int i = 0; i < n; ++i) {
+        kda_status st = check_device_span(sp[i]);
+        if (st != KDA_OK) return st;
+    }
+    return KDA_OK;
+}
+
+kda_status launch_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(KDA_ERR_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH";
+        case KDA_ERR_DEVICE: return "KDA_ERR_DEVICE";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+const char *kda_last_error(void) { return g_last_error; }
+
+int kda_version(void) { return 100; }  // 0.1.0
+
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                         const float *h0, float *o, float *hT, int64_t B, int64_t T, int64_t H, int64_t Dk,
+                         int64_t Dv, kda_dtype in_dtype, float scale, void *stream) {
+    if (B <= 0 || H <= 0 || Dk <= 0 || Dv <= 0 || T < 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "sizes must be positive (T >= 0): B=%lld T=%lld H=%lld Dk=%lld Dv=%lld",
+                    (long long)B, (long long)T, (long long)H, (long long)Dk, (long long)Dv);
+    if (in_dtype != KDA_F32 && in_dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown in_dtype %d", static_cast<int>(in_dtype));
+    if (Dk != Dv || (Dk != 16 && Dk != 128))
+        return fail(KDA_ERR_UNSUPPORTED, "head dims Dk=%lld Dv=%lld: only Dk == Dv in {16, 128} is built",
+                    (long long)Dk, (long long)Dv);
+    if (T > 0 && (!q || !k || !v || !g || !beta || !o))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and o must be non-null when T > 0");
+    if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
+
+    uint64_t n_tok = 1, n_state = 1;
+    if (!mul_ok(n_tok, B) || !mul_ok(n_tok, T) || !mul_ok(n_tok, H) || !mul_ok(n_state, B) ||
+        !mul_ok(n_state, H) || !mul_ok(n_state, Dk) || !mul_ok(n_state, Dv))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "tensor sizes overflow 64 bits");
+    uint64_t n_qk = n_tok, n_v = n_tok;
+    if (!mul_ok(n_qk, Dk) || !mul_ok(n_v, Dv) || n_qk > UINT64_MAX / 8)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "tensor sizes overflow 64 bits");
+    if (B * H * 64 > INT32_MAX) return fail(KDA_ERR_UNSUPPORTED, "B*H too large for one launch");
+    const uint64_t esz = in_dtype == KDA_BF16 ? 2 : 4;
+
+    const Span sp[] = {
+        {"q", q, n_qk * esz}, {"k", k, n_qk * esz},    {"v", v, n_v * esz},         {"g", g, n_qk * 4},
+        {"beta", beta, n_tok * 4}, {"h0", h0, n_state * 4}, {"o", o, n_v * 4}, {"hT", hT, n_state * 4},
+    };
+    constexpr int kO = 6, kHT = 7, kH0 = 5;
+    for (int i = 0; i < 8; ++i) {
+        if (i != kO && overlaps(sp[kO], sp[i]))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "o overlaps %s", sp[i].name);
+    }
+    for (int i = 0; i < 5; ++i) {
+        if (overlaps(sp[kHT], sp[i])) return fail(KDA_ERR_INVALID_ARGUMENT, "hT overlaps %s", sp[i].name);
+    }
+    if (overlaps(sp[kHT], sp[kH0]) && hT != h0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "hT partially overlaps h0 (only an exact alias is allowed)");
+    kda_status st = check_device();
+    if (st != KDA_OK) return st;
+    st = check_spans(sp, 8);
+    if (st != KDA_OK) return st;
+
+    kda::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.hT = hT;
+    a.B = B; a.T = T; a.H = H; a.D = static_cast<int>(Dk);
+    a.bf16 = in_dtype == KDA_BF16;
+    a.scale = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(Dk));
+    if (T == 0 && !hT) return ok();  // nothing to compute or write
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (kda::prefill_mfma_supported(a)) return launch_status(kda::launch_prefill_mfma(a, s), "kda prefill (mfma)");
+    return launch_status(kda::launch_prefill_valu(a, s), "kda prefill (valu)");
+}
+
+kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                           float *state, float *o, int64_t B, int64_t H, int64_t Dk, int64_t Dv,
+                           kda_dtype in_dtype, float scale, void *stream) {
+    if (B <= 0 || H <= 0 || Dk <= 0 || Dv <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "sizes must be positive: B=%lld H=%lld Dk=%lld Dv=%lld",
+                    (long long)B, (long long)H, (long long)Dk, (long long)Dv);
+    if (in_dtype != KDA_F32 && in_dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown in_dtype %d", static_cast<int>(in_dtype));
+    if (Dk != Dv || (Dk != 16 && Dk != 128))
+        return fail(KDA_ERR_UNSUPPORTED, "head dims Dk=%lld Dv=%lld: only Dk == Dv in {16, 128} is built",
+                    (long long)Dk, (long long)Dv);
+    if (!q || !k || !v || !g || !beta || !state || !o)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "every pointer must be non-null");
+    if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
+    uint64_t n_bh = 1, n_state = 1;
+    if (!mul_ok(n_bh, B) || !mul_ok(n_bh, H) || !mul_ok(n_state, B) || !mul_ok(n_state, H) ||
+        !mul_ok(n_state, Dk) || !mul_ok(n_state, Dv) || n_state > UINT64_MAX / 8)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "tensor sizes overflow 64 bits");
+    if (n_bh > static_cast<uint64_t>(INT32_MAX)) return fail(KDA_ERR_UNSUPPORTED, "B*H too large for one launch");
+    const uint64_t esz = in_dtype == KDA_BF16 ? 2 : 4;
+    const Span sp[] = {
+        {"q", q, n_bh * Dk * esz}, {"k", k, n_bh * Dk * esz}, {"v", v, n_bh * Dv * esz},
+        {"g", g, n_bh * Dk * 4},   {"beta", beta, n_bh * 4},  {"state", state, n_state * 4},
+        {"o", o, n_bh * Dv * 4},
+    };
+    for (int i = 0; i < 7; ++i) {
+        for (int j = i + 1; j < 7; ++j) {
+            const bool writes = (i >= 5 || j >= 5);
+            if (writes && overlaps(sp[i], sp[j]))
+                return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps %s", sp[i].name, sp[j].name);
+        }
+    }
+    kda_status st = check_device();
+    if (st != KDA_OK) return st;
+    st = check_spans(sp, 7);
+    if (st != KDA_OK) return st;
+
+    kda::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
+    a.B = B; a.H = H; a.D = static_cast<int>(Dk);
+    a.bf16 = in_dtype == KDA_BF16;
+    a.scale = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(Dk));
+    return launch_status(kda::launch_decode(a, static_cast<hipStream_t>(stream)), "kda decode");
+}
+
+}  // extern "C"

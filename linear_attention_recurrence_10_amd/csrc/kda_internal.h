@@ -1,0 +1,48 @@
+// kda_internal.h -- shared declarations of the HIP library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kChunk = 16;  // tokens per chunk: g_min = -5 keeps exp(+-16*5) inside bf16 range
+
+struct PrefillArgs {
+    const void *q, *k, *v;   // [B,T,H,D] in dtype
+    const float *g;          // [B,T,H,D]
+    const float *beta;       // [B,T,H]
+    const float *h0;         // [B,H,D,D] or null
+    float *o;                // [B,T,H,D]
+    float *hT;               // [B,H,D,D] or null (may equal h0)
+    int64_t B, T, H;
+    int D;
+    bool bf16;
+    float scale;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v;   // [B,H,D]
+    const float *g;          // [B,H,D]
+    const float *beta;       // [B,H]
+    float *state;            // [B,H,D,D], in place
+    float *o;                // [B,H,D]
+    int64_t B, H;
+    int D;
+    bool bf16;
+    float scale;
+};
+
+// Each launcher returns hipSuccess or the launch error; all are asynchronous.
+hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s);
+bool prefill_mfma_supported(const PrefillArgs &a);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+
+// bf16 (stored as raw 16-bit patterns) and fp32 element loads.
+__device__ __forceinline__ float ld_elem(const uint16_t *p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+__device__ __forceinline__ float ld_elem(const float *p, int64_t i) { return p[i]; }
+
+}  // namespace kda

@@ -1,0 +1,126 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, and
+its host-side validation rejects bad arguments before touching any device."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_recurrence_10_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.library_path()):
+        from linear_attention_recurrence_10_amd import build
+        build.build()
+    return kda.library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("kda_chunk_fwd", "kda_decode_step", "kda_status_string", "kda_last_error", "kda_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert kda.version() >= 100
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(1) == b"KDA_ERR_INVALID_ARGUMENT"
+    assert lib.kda_status_string(2) == b"KDA_ERR_UNSUPPORTED"
+    assert lib.kda_status_string(3) == b"KDA_ERR_LAUNCH"
+    assert lib.kda_status_string(4) == b"KDA_ERR_DEVICE"
+
+
+# Host-side validation: each call below fails before any device query, so it is
+# safe without a GPU.  Pointers are fake non-null addresses (never dereferenced).
+P = ctypes.c_void_p(0x1000)
+
+
+def chunk(lib, B=1, T=16, H=1, Dk=128, Dv=128, dtype=1, ptrs=None):
+    p = ptrs or [P] * 8
+    return lib.kda_chunk_fwd(*p, B, T, H, Dk, Dv, dtype, 0.0, None)
+
+
+def decode(lib, B=1, H=1, Dk=128, Dv=128, dtype=1, ptrs=None):
+    p = ptrs or [P] * 7
+    return lib.kda_decode_step(*p, B, H, Dk, Dv, dtype, 0.0, None)
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(T=-1), dict(Dk=0), dict(Dv=-3), dict(dtype=7)])
+def test_chunk_rejects_bad_sizes(lib, kw):
+    assert chunk(lib, **kw) == 1
+    assert lib.kda_last_error() != b""
+
+
+@pytest.mark.parametrize("kw", [dict(Dk=64, Dv=64), dict(Dk=128, Dv=64), dict(Dk=256, Dv=256)])
+def test_chunk_unsupported_dims(lib, kw):
+    assert chunk(lib, **kw) == 2
+
+
+def test_chunk_null_inputs(lib):
+    ptrs = [P] * 8
+    ptrs[0] = None
+    assert chunk(lib, ptrs=ptrs) == 1
+    assert b"non-null" in lib.kda_last_error()
+
+
+def test_chunk_output_overlaps_input(lib):
+    # o at the same address as q
+    ptrs = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(8)]
+    ptrs[6] = ptrs[0]
+    assert chunk(lib, ptrs=ptrs) == 1
+    assert b"o overlaps" in lib.kda_last_error()
+
+
+def test_chunk_partial_state_alias(lib):
+    ptrs = [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(8)]
+    ptrs[7] = ctypes.c_void_p(ptrs[5].value + 64)   # hT = h0 + 16 floats
+    assert chunk(lib, ptrs=ptrs) == 1
+    assert b"partially overlaps" in lib.kda_last_error()
+
+
+def test_chunk_size_overflow(lib):
+    assert chunk(lib, B=1 << 40, T=1 << 30) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=-1), dict(dtype=5)])
+def test_decode_rejects_bad_sizes(lib, kw):
+    assert decode(lib, **kw) == 1
+
+
+def test_decode_unsupported_and_null(lib):
+    assert decode(lib, Dk=32, Dv=32) == 2
+    ptrs = [P] * 7
+    ptrs[5] = None
+    assert decode(lib, ptrs=ptrs) == 1
+
+
+def test_decode_overlap(lib):
+    ptrs = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(7)]
+    ptrs[6] = ptrs[5]   # o == state
+    assert decode(lib, ptrs=ptrs) == 1
+    assert b"overlaps" in lib.kda_last_error()
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 16, 1, 16)
+    with pytest.raises(ValueError):
+        kda.chunk_fwd(x, x, x, x.float(), torch.zeros(1, 16, 1))
