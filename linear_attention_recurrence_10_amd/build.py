@@ -24,6 +24,8 @@ HIPCC_FLAGS = [
     "-fPIC",
     # no packed fp32 instructions (v_pk_fma_f32 and friends) in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep matrix-core results in ordinary VGPRs (no accumulation-register copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 
