@@ -1,9 +1,11 @@
 """Benchmark of the KDA forward hot path on one MI355X.
 
 One step = one chunked prefill over the 64K-token full-width workload
-(B=1, H=56, T=65536, d=128, bf16 q/k/v, fp32 g/beta/o/state) followed by one
+(B=1, H=56, T=65536, d=128, bf16 q/k/v, fp32 g/beta/o/state) and one
 decode step over 256 sequences x 56 heads (fp32 state updated in place).
-Inputs are resident in HBM before timing starts.
+The K prefills run first, then the K decode steps (a decode loop); each
+launch is timed with events on its stream.  Inputs are resident in HBM
+before timing starts.
 
 Prints ONE JSON line on stdout:
   value          prefill tokens/s (B*T / mean prefill kernel time)
@@ -26,9 +28,11 @@ if ROOT not in sys.path:
 
 METRIC = "KDA prefill tokens/s (H=56,d=128,T=64K); decode-step HBM GB/s vs peak"
 HBM_PEAK_GBPS = 8000.0
+COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_prefill_64k_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_recurrence_10_amd", "csrc", f)
-                  for f in ("kda_prefill_valu.hip", "kda_prefill_mfma.hip", "kda_api.cpp")]
+_CSRC = os.path.join(ROOT, "linear_attention_recurrence_10_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in ("kda_prefill_mfma.hip", "kda_internal.h")]
+DECODE_SOURCES = [os.path.join(_CSRC, f) for f in ("kda_decode.hip", "kda_internal.h")]
 
 
 def log(msg):
@@ -48,25 +52,26 @@ def decode_bytes(B, H, D, in_bytes=2):
     return B * H * (2 * 4 * D * D + 3 * D * in_bytes + 4 * D + 4 + 4 * D)
 
 
-def source_hash():
+def source_hash(files=None):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (KERNEL_SOURCES if files is None else files):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes per prefill launch from committed rocprofv3 counter runs, or
-    None when they are missing or were taken on different kernel sources."""
+def load_traffic(kernel="prefill"):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None
+    when they are missing or were taken on different kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_src_sha") != source_hash():
+    sha = t.get("kernel_src_sha") if kernel == "prefill" else t.get("decode_src_sha")
+    if sha != source_hash(KERNEL_SOURCES if kernel == "prefill" else DECODE_SOURCES):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return (t.get(kernel) or {}).get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(target_s: float):
@@ -108,6 +113,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain device copy of %d bytes first (for the traffic counters)" % (1 << 30))
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -142,34 +149,58 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def prefill(ev=None):
         if ev:
             ev[0].record(stream)
         kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], None, o=o, hT=hT, stream=stream)
         if ev:
             ev[1].record(stream)
-        if d is not None:
-            kda.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], o=od, stream=stream)
-            if ev:
-                ev[2].record(stream)
+
+    def decode(ev=None):
+        if ev:
+            ev[0].record(stream)
+        kda.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], o=od, stream=stream)
+        if ev:
+            ev[1].record(stream)
+
+    if args.copy_calibration:
+        # a plain device copy of known size: the reference that scales the
+        # FETCH_SIZE / WRITE_SIZE counters to bytes
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
-        step()
+        prefill()
+        if d is not None:
+            decode()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # prefill steps, then decode steps (a decode loop), each timed per launch
+    # with events on the stream the kernels run on
+    pre_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    dec_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     log("timing %d steps" % args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        prefill(pre_ev[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    pre_ms = [e[0].elapsed_time(e[1]) for e in events]
-    dec_ms = [e[1].elapsed_time(e[2]) for e in events] if d is not None else []
+    wall_pre = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    if d is not None:
+        for i in range(args.steps):
+            decode(dec_ev[i])
+    torch.cuda.synchronize()
+    wall_dec = time.perf_counter() - t0
+    pre_ms = [e[0].elapsed_time(e[1]) for e in pre_ev]
+    dec_ms = [e[0].elapsed_time(e[1]) for e in dec_ev] if d is not None else []
     pre_avg = sum(pre_ms) / len(pre_ms)
-    ms_per_step = 1e3 * wall / args.steps
+    ms_per_step = 1e3 * (wall_pre + wall_dec) / args.steps
     log("prefill avg %.3f ms (min %.3f), decode avg %s ms, wall/step %.3f ms" % (
         pre_avg, min(pre_ms), ("%.3f" % (sum(dec_ms) / len(dec_ms))) if dec_ms else "-", ms_per_step))
 
@@ -188,7 +219,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "T": cfg.T, "d_k": cfg.D, "d_v": cfg.D,
                    "chunk": kda_inputs.CHUNK, "inputs": "q,k,v bf16; g,beta fp32; o,state fp32",
@@ -203,7 +234,8 @@ def main():
         dec_avg = sum(dec_ms) / len(dec_ms)
         dg = dbytes / (dec_avg * 1e-3) / 1e9
         result["decode"] = {"workload": dcfg.name, "ms": dec_avg, "achieved": dg, "peak": HBM_PEAK_GBPS,
-                            "unit": "GB/s", "frac": dg / HBM_PEAK_GBPS, "alg_bytes_per_launch": dbytes}
+                            "unit": "GB/s", "frac": dg / HBM_PEAK_GBPS, "alg_bytes_per_launch": dbytes,
+                            "traffic": load_traffic("decode")}
     if not args.no_cpu_baseline:
         del x, o, hT
         log("cpu baseline (oracle), ~%.0f s" % args.cpu_seconds)

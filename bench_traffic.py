@@ -1,0 +1,129 @@
+"""Turn rocprofv3 runs of bench.py into the per-launch HBM traffic figures.
+
+Inputs are three rocprofv3 output directories made with the commands below
+(each one a separate run; counters never share a run with other tracing):
+
+  rocprofv3 --kernel-trace --stats --output-format csv -d DIR_T -o trace -- \\
+      python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR_F -o fetch -- \\
+      python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR_W -o write -- \\
+      python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration
+
+FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
+counter reads for the runtime's plain copy of COPY_BYTES bytes, so that a
+copy counts exactly COPY_BYTES read and COPY_BYTES written.  Writes
+OUT/kda_prefill_64k_traffic.json (read by bench.py while the kernel sources
+are unchanged) and OUT/kda_prefill_64k_decode_b256_rocprof.md.
+
+usage: python3 bench_traffic.py DIR_T DIR_F DIR_W OUT
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import json
+import os
+import statistics
+import sys
+
+import bench
+
+PREFILL = "prefill_mfma_kernel"
+DECODE = "decode_kernel"
+COPY = "copyBuffer"
+
+
+def _csv(d, suffix):
+    files = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+    if not files:
+        raise SystemExit("no *%s under %s" % (suffix, d))
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def per_dispatch(d, counter):
+    """{dispatch id: (kernel name, summed counter value)} for one counter run."""
+    out = {}
+    for r in _csv(d, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        k = int(r["Dispatch_Id"])
+        name, v = out.get(k, (r["Kernel_Name"], 0.0))
+        out[k] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def calibration_copy(disp):
+    """The copy bench.py --copy-calibration runs right before the first KDA
+    kernel (earlier copies belong to input generation)."""
+    first_kda = min(k for k, (name, _) in disp.items() if PREFILL in name or DECODE in name)
+    copies = [k for k, (name, _) in disp.items() if COPY in name and k < first_kda]
+    if not copies:
+        raise SystemExit("copy calibration dispatch not found")
+    return disp[max(copies)][1]
+
+
+def mean_for(disp, key):
+    vals = [v for name, v in disp.values() if key in name]
+    return statistics.mean(vals) if vals else None, len(vals)
+
+
+def main(dt, df, dw, out):
+    fetch = per_dispatch(df, "FETCH_SIZE")
+    write = per_dispatch(dw, "WRITE_SIZE")
+    copy_f = calibration_copy(fetch)
+    copy_w = calibration_copy(write)
+    kib = bench.COPY_BYTES / 1024.0
+    sf, sw = kib / copy_f, kib / copy_w
+    res = {"copy_bytes": bench.COPY_BYTES, "fetch_scale": sf, "write_scale": sw,
+           "kernel_src_sha": bench.source_hash(), "decode_src_sha": bench.source_hash(bench.DECODE_SOURCES)}
+    for key, tag in ((PREFILL, "prefill"), (DECODE, "decode")):
+        f, nf = mean_for(fetch, key)
+        w, nw = mean_for(write, key)
+        res[tag] = {"fetch_kib_raw": f, "write_kib_raw": w, "dispatches": [nf, nw],
+                    "fetch_bytes": f * 1024 * sf, "write_bytes": w * 1024 * sw,
+                    "hbm_bytes_per_launch": f * 1024 * sf + w * 1024 * sw}
+    res["hbm_bytes_per_launch"] = res["prefill"]["hbm_bytes_per_launch"]
+    stats = _csv(dt, "kernel_stats.csv")
+    res["kernel_stats"] = [{"name": r["Name"][:90], "calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
+                            "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])}
+                           for r in stats if PREFILL in r["Name"] or DECODE in r["Name"] or COPY in r["Name"]]
+    os.makedirs(out, exist_ok=True)
+    with open(os.path.join(out, "kda_prefill_64k_traffic.json"), "w") as f:
+        json.dump(res, f, indent=1)
+    alg_p = bench.prefill_bytes(1, 65536, 56, 128)
+    alg_d = bench.decode_bytes(256, 56, 128)
+    lines = ["# rocprofv3: KDA prefill (B=1 H=56 T=65536 d=128) and decode (B=256 H=56 d=128)", "",
+             "Commands (from the repository root):", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d DIR_T -o trace -- "
+             "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline",
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR_F -o fetch -- "
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration",
+             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR_W -o write -- "
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration",
+             "    python3 bench_traffic.py DIR_T DIR_F DIR_W profiles", "",
+             "Kernel source hash: prefill %s, decode %s" % (res["kernel_src_sha"], res["decode_src_sha"]), "",
+             "## Kernel trace (--stats)", "", "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in res["kernel_stats"]:
+        lines.append("| %s | %d | %.1f | %.1f | %.1f |" % (r["name"], r["calls"], r["avg_ns"] / 1e3,
+                                                          r["min_ns"] / 1e3, r["max_ns"] / 1e3))
+    lines += ["", "## HBM traffic (FETCH_SIZE, WRITE_SIZE)", "",
+              "Copy calibration: %d bytes copied; raw FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB; "
+              "scale factors %.4f (fetch), %.4f (write)." % (bench.COPY_BYTES, copy_f, copy_w, sf, sw), "",
+              "| kernel | raw fetch KiB | raw write KiB | scaled bytes | algorithmic bytes | ratio |",
+              "|---|---|---|---|---|---|"]
+    for tag, alg in (("prefill", alg_p), ("decode", alg_d)):
+        r = res[tag]
+        lines.append("| %s | %.0f | %.0f | %.4g | %.4g | %.3f |" % (tag, r["fetch_kib_raw"], r["write_kib_raw"],
+                                                                  r["hbm_bytes_per_launch"], alg,
+                                                                  r["hbm_bytes_per_launch"] / alg))
+    with open(os.path.join(out, "kda_prefill_64k_decode_b256_rocprof.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({k: res[k] for k in ("fetch_scale", "write_scale", "hbm_bytes_per_launch")}))
+
+
+if __name__ == "__main__":
+    if len(sys.argv) != 5:
+        raise SystemExit(__doc__)
+    main(*sys.argv[1:])

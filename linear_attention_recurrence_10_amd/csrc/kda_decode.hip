@@ -9,9 +9,14 @@
 // written once; everything else is a few hundred bytes per head, so the
 // kernel is a streaming pass bounded by HBM bandwidth.
 //
-// One work-group per (batch, head).  Thread (rg, jq) holds the float4 column
-// quad jq of rows rg, rg + RG, ... in registers; the two column reductions
-// (r, p) and k . q are combined across row groups through LDS.
+// Persistent work-groups walk the (batch, head) list with a stride of the
+// grid size.  Thread (rg, jq) holds the float4 column quad jq of rows
+// rg, rg + RG, ... of one state in registers; the next head's state is loaded
+// while the current one is reduced and written back, so reads and writes of
+// consecutive heads overlap.  The two column reductions (r, p) and k . q are
+// combined across row groups through LDS.
+#include <atomic>
+
 #include "kda_internal.h"
 
 namespace kda {
@@ -21,8 +26,8 @@ using f32x4 = float __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct DecodeShape {
-    static constexpr int NQ = D / 4;                               // float4 quads per row
-    static constexpr int NT = (NQ * D < 256) ? NQ * D : 256;       // threads per head
+    static constexpr int NQ = D / 4;                                // float4 quads per row
+    static constexpr int NT = (NQ * D < 512) ? NQ * D : 512;        // threads per work-group
     static constexpr int RG = NT / NQ;                              // row groups
     static constexpr int RPT = D / RG;                              // rows per thread
 };
@@ -30,74 +35,107 @@ struct DecodeShape {
 template <int D, typename InT>
 __global__ __launch_bounds__(DecodeShape<D>::NT) void decode_kernel(DecodeArgs a) {
     using Sh = DecodeShape<D>;
-    constexpr int NQ = Sh::NQ, NT = Sh::NT, RG = Sh::RG, RPT = Sh::RPT;
-    static_assert(RG * RPT == D && NQ * RG == NT, "bad decode tiling");
+    constexpr int NQ = Sh::NQ, RG = Sh::RG, RPT = Sh::RPT;
+    static_assert(RG * RPT == D && NQ * RG == Sh::NT, "bad decode tiling");
 
-    __shared__ f32x4 sR[RG][NQ];
-    __shared__ f32x4 sP[RG][NQ];
-    __shared__ float sKQ[RG];
-    __shared__ f32x4 sE[NQ];
+    __shared__ f32x4 sR[2][RG][NQ];
+    __shared__ f32x4 sP[2][RG][NQ];
+    __shared__ float sKQ[2][RG];
+    __shared__ f32x4 sE[2][NQ];
 
     const int tid = threadIdx.x;
     const int jq = tid % NQ;
     const int rg = tid / NQ;
-    const int64_t bh = blockIdx.x;
-
-    const InT *q = static_cast<const InT *>(a.q) + bh * D;
-    const InT *k = static_cast<const InT *>(a.k) + bh * D;
-    const InT *v = static_cast<const InT *>(a.v) + bh * D;
-    const float *g = a.g + bh * D;
-    f32x4 *S = reinterpret_cast<f32x4 *>(a.state + bh * static_cast<int64_t>(D) * D);
+    const int64_t BH = a.B * a.H;
+    int64_t bh = blockIdx.x;
+    if (bh >= BH) return;
 
     f32x4 s[RPT];
+    {
+        const f32x4 *S = reinterpret_cast<const f32x4 *>(a.state + bh * static_cast<int64_t>(D) * D);
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) s[m] = __builtin_nontemporal_load(&S[(rg + RG * m) * NQ + jq]);
-
-    float kk[RPT];
-    f32x4 r4 = {0.f, 0.f, 0.f, 0.f}, p4 = r4;
-    float kq = 0.f;
-#pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int i = rg + RG * m;
-        const float ai = __expf(g[i]);
-        const float ki = ld_elem(k, i);
-        const float qi = ld_elem(q, i);
-        kk[m] = ki;
-        s[m] *= ai;
-        r4 += ki * s[m];
-        p4 += qi * s[m];
-        kq += ki * qi;
+        for (int m = 0; m < RPT; ++m) s[m] = __builtin_nontemporal_load(&S[(rg + RG * m) * NQ + jq]);
     }
-    sR[rg][jq] = r4;
-    sP[rg][jq] = p4;
-    if (jq == 0) sKQ[rg] = kq;
-    __syncthreads();
-
-    if (rg == 0) {
-        f32x4 rt = {0.f, 0.f, 0.f, 0.f}, pt = rt;
-        float kqt = 0.f;
-        for (int j = 0; j < RG; ++j) {
-            rt += sR[j][jq];
-            pt += sP[j][jq];
-            kqt += sKQ[j];
+    for (int par = 0; bh < BH; bh += gridDim.x, par ^= 1) {
+        const int64_t nb = bh + gridDim.x;
+        f32x4 sn[RPT];
+        if (nb < BH) {  // next head's state, in flight while this head is processed
+            const f32x4 *Sn = reinterpret_cast<const f32x4 *>(a.state + nb * static_cast<int64_t>(D) * D);
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) sn[m] = __builtin_nontemporal_load(&Sn[(rg + RG * m) * NQ + jq]);
         }
-        const float bt = a.beta[bh];
-        const int c0 = jq * 4;
-        const f32x4 vv = {ld_elem(v, c0 + 0), ld_elem(v, c0 + 1), ld_elem(v, c0 + 2), ld_elem(v, c0 + 3)};
-        const f32x4 e = bt * (vv - rt);
-        sE[jq] = e;
-        reinterpret_cast<f32x4 *>(a.o + bh * D)[jq] = a.scale * (pt + e * kqt);
-    }
-    __syncthreads();
+        const InT *q = static_cast<const InT *>(a.q) + bh * D;
+        const InT *k = static_cast<const InT *>(a.k) + bh * D;
+        const InT *v = static_cast<const InT *>(a.v) + bh * D;
+        const float *g = a.g + bh * D;
+        f32x4 *S = reinterpret_cast<f32x4 *>(a.state + bh * static_cast<int64_t>(D) * D);
 
-    const f32x4 e = sE[jq];
+        float kk[RPT];
+        f32x4 r4 = {0.f, 0.f, 0.f, 0.f}, p4 = r4;
+        float kq = 0.f;
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) __builtin_nontemporal_store(s[m] + kk[m] * e, &S[(rg + RG * m) * NQ + jq]);
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + RG * m;
+            const float ai = __expf(g[i]);
+            const float ki = ld_elem(k, i);
+            const float qi = ld_elem(q, i);
+            kk[m] = ki;
+            s[m] *= ai;
+            r4 += ki * s[m];
+            p4 += qi * s[m];
+            kq += ki * qi;
+        }
+        sR[par][rg][jq] = r4;
+        sP[par][rg][jq] = p4;
+        if (jq == 0) sKQ[par][rg] = kq;
+        __syncthreads();
+
+        if (rg == 0) {
+            f32x4 rt = {0.f, 0.f, 0.f, 0.f}, pt = rt;
+            float kqt = 0.f;
+            for (int j = 0; j < RG; ++j) {
+                rt += sR[par][j][jq];
+                pt += sP[par][j][jq];
+                kqt += sKQ[par][j];
+            }
+            const float bt = a.beta[bh];
+            const int c0 = jq * 4;
+            const f32x4 vv = {ld_elem(v, c0 + 0), ld_elem(v, c0 + 1), ld_elem(v, c0 + 2), ld_elem(v, c0 + 3)};
+            const f32x4 e = bt * (vv - rt);
+            sE[par][jq] = e;
+            reinterpret_cast<f32x4 *>(a.o + bh * D)[jq] = a.scale * (pt + e * kqt);
+        }
+        __syncthreads();
+
+        const f32x4 e = sE[par][jq];
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) __builtin_nontemporal_store(s[m] + kk[m] * e, &S[(rg + RG * m) * NQ + jq]);
+        if (nb < BH) {
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) s[m] = sn[m];
+        }
+    }
+}
+
+// Work-groups resident at once: four per compute unit keeps enough state
+// loads in flight to stream at close to the copy rate.
+std::atomic<int> g_cus[64];
+
+int decode_grid(int64_t BH) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        g_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    const int64_t g = static_cast<int64_t>(n) * 4;
+    return static_cast<int>(BH < g ? BH : g);
 }
 
 template <int D>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
-    dim3 grid(static_cast<unsigned>(a.B * a.H)), block(DecodeShape<D>::NT);
+    dim3 grid(static_cast<unsigned>(decode_grid(a.B * a.H))), block(DecodeShape<D>::NT);
     if (a.bf16)
         hipLaunchKernelGGL((decode_kernel<D, uint16_t>), grid, block, 0, s, a);
     else
