@@ -2,9 +2,9 @@
 //
 // Handles bf16 q/k/v with d_k = d_v = 128 (fp32 gates, state and output).
 // One work-group per (batch, head, 32-column value slice): 4 slices per head,
-// so a 56-head sequence runs on 224 work-groups.  The slices of one head are
-// placed on the same XCD (blockIdx -> XCD is round-robin), so their repeated
-// reads of q, k, g hit that XCD's L2.
+// so a 56-head sequence runs on 224 work-groups, one per compute unit.  The
+// slices of one head are placed on the same XCD (blockIdx -> XCD is
+// round-robin), so their repeated reads of q, k, g hit that XCD's L2.
 //
 // Chunk form for a 16-token chunk with start state S0 (rows = key channels),
 // per-channel cumulative log-decay gamma_r = g_1 + ... + g_r and
@@ -24,25 +24,33 @@
 // in three bf16 passes (x = x_hi + x_lo; a*b ~ a_hi b_hi + a_hi b_lo +
 // a_lo b_hi) with fp32 accumulation, which keeps fp32-level accuracy.
 //
-// Work split inside a work-group (4 waves): wave w owns key channels
-// [32w, 32w + 32) = 16-channel tiles 2w and 2w + 1.  It loads and scales
-// those channels, forms their contributions to the 16x16 Gram matrices and to
-// X, Y, and holds the matching 32 rows of the state slice in registers.
-// Partial Grams and partial X, Y are summed across waves through LDS; wave 0
-// solves the triangular system.
+// Work split inside a work-group: 8 waves, two per SIMD, in two roles.
+//  * k-side waves 0..3 work ahead of the state: wave kw takes key channels
+//    [32 kw, 32 kw + 32) of chunk n + 2 (gate prefix sums, exponentials, the
+//    scaled and split operands, its partial Grams) and solves M of chunk n + 1.
+//    Everything they produce goes to LDS: a ring of three chunks of operands,
+//    double-buffered Grams, M and P.
+//  * state waves 4..7 carry the state slice: wave (row half rh, column tile
+//    ct) holds state rows [64 rh, 64 rh + 64) x columns 16 ct .. 16 ct + 15
+//    in registers and runs the state part of chunk n.  The two row halves of
+//    a column tile exchange their partial X, Y through LDS with a flag
+//    handshake; both then form the same U for their own rows.
+// One work-group barrier per chunk hands the k-side of later chunks to the
+// state waves; a k-side wave and a state wave share each SIMD, so one's
+// vector work fills the other's matrix-core and LDS latency.
 //
 // Operand layouts (lane l, row group g = l / 16, n = l % 16):
 //   16x16x16 (bf16_1k):  A[m = n][k = 4g + i],  B[k = 4g + i][col = n]
 //   16x16x32 (bf16):     A[m = n][k = 8g + j],  B[k = 8g + j][col = n]
 //   result:              C[row = 4g + i][col = n]
 // "Token per lane": lane (n, g) holds token n of the chunk and, in slot j of
-// an 8-wide operand, key channel 16 (2w) + 4g + j (j < 4) or
-// 16 (2w + 1) + 4g + j - 4 (j >= 4).  This is the operand layout of every
+// an 8-wide operand of quarter kw, key channel 32 kw + 4g + j (j < 4) or
+// 32 kw + 16 + 4g + j - 4 (j >= 4).  This is the operand layout of every
 // contraction over channels (X, Y, the Grams); the state rows are kept in the
-// result layout of two 16-row tiles, which lists the same channels in the
-// same slots.  q, k, g are loaded straight into it with 8- and 16-byte loads,
-// and the cumulative decay over tokens is a prefix sum across the 16 lanes of
-// a row (DPP row shifts).  Kd, the operand of the contraction over tokens,
+// result layout of 16-row tiles, which lists the same channels in the same
+// slots.  q, k, g are loaded straight into it with 8- and 16-byte loads, and
+// the cumulative decay over tokens is a prefix sum across the 16 lanes of a
+// row (DPP row shifts).  Kd, the operand of the contraction over tokens,
 // needs "channel per lane" (channel n, tokens 4g .. 4g + 3): a 16x16x16
 // product with the identity converts it exactly (its inputs are bf16).  The
 // Grams are formed transposed (Kh Kb^T, Kh Qb^T), so their result layout is
@@ -67,6 +75,9 @@ constexpr int kD = 128;     // head dimension (d_k = d_v)
 constexpr int kDVS = 32;    // value columns per work-group
 constexpr int kNV = kD / kDVS;
 constexpr int kC = kChunk;  // 16
+constexpr int kThreads = 512;
+constexpr int kRing = 3;    // chunks of k-side operands in flight
+constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
@@ -83,15 +94,28 @@ struct Sp8 {
     bf16x8 hi, lo;
 };
 
-// x = hi + lo with hi = x truncated to bf16 (its upper 16 bits, so x - hi is
-// exact) and lo = bf16(x - hi) rounded to nearest: |x - hi - lo| <= 2^-16 |x|.
-// Per pair of values: one byte permute packs the two hi halves, one
-// conversion packs the two lo values.
+// A packed bf16 pair held in a scalar register.  The constant goes through
+// an empty asm so that it is not folded into an inline constant: the
+// compiler encodes the pair (-1, 0) as the inline constant -1.0 for the bf16
+// dot product, and the hardware was observed to compute wrong remainders
+// from that encoding (a literal or a register operand gives exact ones).
+__device__ __forceinline__ bf16x2 sgpr_pair(uint32_t bits) {
+    asm("" : "+s"(bits));
+    return __builtin_bit_cast(bf16x2, bits);
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), both rounded to
+// nearest: |x - hi - lo| <= 2^-16 |x|.  x - hi is exact in fp32; a bf16 dot
+// product with (-1, 0) forms it in one instruction (-hi + x).  Per pair of
+// values: one conversion packs the two hi halves, two dot products give the
+// remainders, one conversion packs the two lo values.
 __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t &hi, uint32_t &lo) {
-    const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
-    hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);  // [upper half of u0, upper half of u1]
-    const float l0 = x0 - __uint_as_float(u0 & 0xffff0000u);
-    const float l1 = x1 - __uint_as_float(u1 & 0xffff0000u);
+    const bf16x2 h = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
+    const bf16x2 m0 = sgpr_pair(0x0000bf80u);  // (-1, 0)
+    const bf16x2 m1 = sgpr_pair(0xbf800000u);  // (0, -1)
+    const float l0 = __builtin_amdgcn_fdot2_f32_bf16(h, m0, x0, false);
+    const float l1 = __builtin_amdgcn_fdot2_f32_bf16(h, m1, x1, false);
+    hi = __builtin_bit_cast(uint32_t, h);
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){l0, l1}, bf16x2));
 }
 __device__ __forceinline__ Sp4 split4(f32x4 x) {
@@ -108,10 +132,6 @@ __device__ __forceinline__ Sp8 split8(const float (&x)[8]) {
                __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]})};
 }
 
-__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-__device__ __forceinline__ Sp8 cat8(Sp4 a, Sp4 b) { return Sp8{cat8(a.hi, b.hi), cat8(a.lo, b.lo)}; }
 __device__ __forceinline__ bf16x4 first4(bf16x8 x) { return __builtin_shufflevector(x, x, 0, 1, 2, 3); }
 __device__ __forceinline__ bf16x4 last4(bf16x8 x) { return __builtin_shufflevector(x, x, 4, 5, 6, 7); }
 
@@ -135,10 +155,9 @@ __device__ __forceinline__ f32x4 mm16(const Sp4 &a, const Sp4 &b, f32x4 c) {
 
 // bf16 values (exact) from an fp32 result vector.
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
-    bf16x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = static_cast<__bf16>(x[i]);
-    return r;
+    const bf16x2 a = __builtin_convertvector((f32x2){x[0], x[1]}, bf16x2);
+    const bf16x2 b = __builtin_convertvector((f32x2){x[2], x[3]}, bf16x2);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3);
 }
 
 // "token per lane" -> "channel per lane" for one 16x16 bf16 tile, exact.
@@ -159,16 +178,6 @@ template <int U>
 __device__ __forceinline__ float row_bcast(float x) {  // lane U of the row to the whole row
     return dpp_move<0x150 + U>(x);
 }
-// Inclusive prefix sum over the 16 lanes of each row (lanes shifted in from
-// outside the row read 0).
-__device__ __forceinline__ float row_prefix_sum(float x) {
-    x += dpp_move<0x111>(x);  // row_shr:1
-    x += dpp_move<0x112>(x);  // row_shr:2
-    x += dpp_move<0x114>(x);  // row_shr:4
-    x += dpp_move<0x118>(x);  // row_shr:8
-    return x;
-}
-
 // Right-looking forward substitution for one column of (I + A)^-1: lane
 // (row r = n, group g) holds X[r][s] for one column s per 16-lane row.  At
 // pivot u every row subtracts A[r][u] times row u; row u of the same column
@@ -183,268 +192,284 @@ __device__ __forceinline__ void tri_pivots(float &x, const float (&ar)[kC]) {
     }
 }
 
-// One chunk's raw inputs for one lane: q, k (4 bf16 per tile) and g (4 fp32
-// per tile) of token n in the "token per lane" layout, beta of token n, and v
-// in the result layout (token 4g + i, value column 16c + n of the slice).
-struct RawChunk {
+// One chunk's k-side operands in the lane order the state waves read them
+// (every access is lane-contiguous).
+struct Ops {
+    bf16x8 qk[2][4][2][64];  // [Qb, Kb][32-channel quarter][hi, lo][lane], token per lane
+    bf16x4 kdt[8][2][64];    // [16-channel tile][hi, lo][lane], Kd channel per lane
+    f32x4 eC[kD / 4];        // e^gamma_C of channels 4i .. 4i + 3
+};
+
+struct Smem {
+    Ops ops[kRing];
+    f32x4 gram[2][4][2][64];      // partial Grams [parity][k-side wave][A, P][lane]
+    f32x4 arow[4][kC][5];         // summed, masked A per k-side wave; rows padded to 80 bytes
+    alignas(16) float M[2][kC][20];  // M = (I + A)^-1 diag(beta) [parity][row][column], padded rows
+    alignas(16) float P[2][kC][20];  // P [parity][row][column], padded rows
+    float beta[2][kC];
+    f32x4 xy[2][2][2][64];        // partial X, Y [row half][X, Y][column tile][lane]
+    uint32_t flag[2][2];          // state-wave handshake [column tile][row half]
+};
+
+// Raw inputs of one chunk for a k-side lane: q, k (4 bf16 per 16-channel
+// tile) and g (4 fp32 per tile) of token n in the "token per lane" layout,
+// and beta of token n.
+struct KRaw {
     u32x2 q[2], k[2];
     f32x4 g[2];
-    uint16_t v[2][4];
     float beta;
 };
 
-// Loop-invariant element offsets of this lane's loads, relative to the first
-// token row of the chunk for this (batch, head).
-struct LaneOffsets {
-    int tok[2];   // token n, channels 16 (2w + tt) + 4g .. + 3
-    int v[2][4];  // token 4g + i, column col0 + 16c + n
-};
-
-__device__ __forceinline__ LaneOffsets lane_offsets(int64_t H, int w, int grp, int n16, int col0) {
-    LaneOffsets o;
-    const int HD = static_cast<int>(H) * kD;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) o.tok[tt] = n16 * HD + 16 * (2 * w + tt) + 4 * grp;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o.v[c][i] = (4 * grp + i) * HD + col0 + 16 * c + n16;
-    }
-    return o;
-}
-
 // Loads never branch per element and never leave the sequence: in a last,
-// partial chunk the token index is clamped.  Offsets are unsigned 32-bit
-// values added to a wave-uniform 64-bit base.
-__device__ __forceinline__ void load_raw(RawChunk &r, const PrefillArgs &a, int64_t t0, int64_t b, int64_t h,
-                                         const LaneOffsets &off, int grp, int n16) {
+// partial chunk the token index is clamped.  Offsets are unsigned 32-bit byte
+// offsets (16 tokens of a row of H heads stay below 2^31 bytes for the head
+// counts this kernel accepts) added to a wave-uniform 64-bit base.
+__device__ __forceinline__ void load_kraw(KRaw &r, const PrefillArgs &a, int64_t t0, int64_t b, int64_t h, int kw,
+                                          int grp, int n16) {
     const int64_t T = a.T, H = a.H;
     const int64_t row0 = (b * T + t0) * H + h;  // token row of the chunk start (wave uniform)
+    const int HD = static_cast<int>(H) * kD;
+    const int tok = (t0 + kC <= T) ? n16 : min(n16, static_cast<int>(T - t0) - 1);
+    const uint32_t e0 = static_cast<uint32_t>(tok * HD + 32 * kw + 4 * grp);
     const char *gb = reinterpret_cast<const char *>(a.g + row0 * kD);
     const char *qb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.q) + row0 * kD);
     const char *kb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k) + row0 * kD);
-    const char *vb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.v) + row0 * kD);
-    const char *betab = reinterpret_cast<const char *>(a.beta + row0);
-    const int64_t rem = T - t0;
-    const int HD = static_cast<int>(H) * kD;
-    int tok_shift = 0, beta_tok = n16;
-    int v_shift[4] = {0, 0, 0, 0};
-    if (rem < kC) {
-        const int last = static_cast<int>(rem) - 1;
-        beta_tok = min(n16, last);
-        tok_shift = (beta_tok - n16) * HD;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v_shift[i] = (min(4 * grp + i, last) - (4 * grp + i)) * HD;
-    }
-    // element offsets are < 2^31 / 4, so the byte offsets fit in 32 bits
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-        const uint32_t e = static_cast<uint32_t>(off.tok[tt] + tok_shift);
+        const uint32_t e = e0 + 16u * tt;
         r.q[tt] = *reinterpret_cast<const u32x2 *>(qb + 2u * e);
         r.k[tt] = *reinterpret_cast<const u32x2 *>(kb + 2u * e);
         r.g[tt] = *reinterpret_cast<const f32x4 *>(gb + 4u * e);
     }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            r.v[c][i] = *reinterpret_cast<const uint16_t *>(vb + 2u * static_cast<uint32_t>(off.v[c][i] + v_shift[i]));
-    }
-    r.beta = *reinterpret_cast<const float *>(betab + 4u * static_cast<uint32_t>(beta_tok * static_cast<int>(H)));
+    r.beta = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(a.beta + row0) +
+                                              4u * static_cast<uint32_t>(tok * static_cast<int>(H)));
 }
 
-// Shared memory, double-buffered by chunk parity: the k-side of chunk n + 1
-// and the state part of chunk n run between the same two barriers.
-struct Smem {
-    f32x4 gram[2][4][2][kC][4];  // partial Grams [parity][wave][A/P][row][column group]
-    f32x4 xy[2][4][2][2][kC][4];  // partial X, Y [parity][wave][X/Y][col tile][column][token group]
-    f32x4 A[4][kC][4];            // per-wave copy of the summed A (beta applied, strict lower)
-    float M[2][kC][kC];           // M = (I + A)^-1 diag(beta) [parity][row][column]
-    float beta[2][kC];
+// Values of one chunk for a state lane: token 4g + i, value column `col`.
+__device__ __forceinline__ void load_v(uint16_t (&v)[4], const PrefillArgs &a, int64_t t0, int64_t b, int64_t h,
+                                       int col, int grp) {
+    const int64_t T = a.T, H = a.H;
+    const int64_t row0 = (b * T + t0) * H + h;
+    const char *vb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.v) + row0 * kD);
+    const int HD = static_cast<int>(H) * kD;
+    const int last = (t0 + kC <= T) ? kC - 1 : static_cast<int>(T - t0) - 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = min(4 * grp + i, last);
+        v[i] = *reinterpret_cast<const uint16_t *>(vb + 2u * static_cast<uint32_t>(tok * HD + col));
+    }
+}
+
+// Unpacked inputs of one chunk for a k-side lane (channel slot j of token n).
+struct KIn {
+    float g[8], q[8], k[8];
+    float beta;
 };
 
-// Everything of one chunk that depends only on its own inputs (not on the
-// state), kept in registers from the iteration that computes it to the one
-// that uses it.
-struct KSide {
-    Sp8 Qb, Kb;     // "token per lane" split operands of X = Kb S0 and Y = Qb S0
-    Sp4 KdT[2];     // "channel per lane" split Kd of the state update, per tile
-    float eC[8];    // e^gamma_C of the lane's 8 state rows
-    f32x4 v[2];     // values, token 4g + i, column 16c + n (masked)
-    float beta;     // beta of token n (masked)
-};
-
-// K-side of the chunk starting at t0: consumes the raw inputs in `raw`, then
-// issues the next chunk's loads into the same registers (no register copy,
-// so nothing waits on them), and leaves the partial Grams of this wave's
-// channels in LDS.
+// K-side, first part, for the chunk starting at t0: unpacks the raw inputs in
+// `raw` and then issues the loads of the chunk starting at t_next into the
+// same registers.
 // Tokens past the end of the sequence become identity steps: their gate is
 // set to 0 and their beta to 0.  That zeroes their rows and columns of A and
 // M, hence their rows of U, so their (finite) q, k and v never contribute.
-__device__ __forceinline__ void kside(const PrefillArgs &a, Smem &sm, RawChunk &raw, int64_t t0, bool more,
-                                      int64_t b, int64_t h, const LaneOffsets &off, int par, int w, int grp,
-                                      int n16, const bf16x4 &ident, KSide &ks) {
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    const bool tok_ok = t0 + n16 < a.T;
-    float gv[8], qv[8], kv[8];
+__device__ __forceinline__ void kside_in(const PrefillArgs &a, KRaw &raw, KIn &in, int64_t t0, int64_t t_next,
+                                         int64_t b, int64_t h, int kw, int grp, int n16) {
+    in.beta = raw.beta;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) gv[4 * tt + i] = tok_ok ? raw.g[tt][i] : 0.f;
+        for (int i = 0; i < 4; ++i) in.g[4 * tt + i] = raw.g[tt][i];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const uint32_t qp = raw.q[tt][p], kp = raw.k[tt][p];
-            qv[4 * tt + 2 * p] = bf16_lo(qp);
-            qv[4 * tt + 2 * p + 1] = bf16_hi(qp);
-            kv[4 * tt + 2 * p] = bf16_lo(kp);
-            kv[4 * tt + 2 * p + 1] = bf16_hi(kp);
+            in.q[4 * tt + 2 * p] = bf16_lo(qp);
+            in.q[4 * tt + 2 * p + 1] = bf16_hi(qp);
+            in.k[4 * tt + 2 * p] = bf16_lo(kp);
+            in.k[4 * tt + 2 * p + 1] = bf16_hi(kp);
         }
     }
-    ks.beta = tok_ok ? raw.beta : 0.f;
+    if (t0 + kC > a.T) {  // last, partial chunk (wave-uniform test)
+        if (t0 + n16 >= a.T) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ks.v[c][i] = bf16_bits(raw.v[c][i]);
+            for (int j = 0; j < 8; ++j) in.g[j] = 0.f;
+            in.beta = 0.f;
+        }
     }
-    if (more) load_raw(raw, a, t0 + kC, b, h, off, grp, n16);
+    load_kraw(raw, a, t_next, b, h, kw, grp, n16);
+}
 
+// K-side, second part: this quarter's operands of the chunk go to `op`, its
+// partial Grams and beta to the `par` buffers.
+__device__ __forceinline__ void kside(Smem &sm, Ops &op, const KIn &in, int par, int kw, int grp, int n16, int lane,
+                                      const bf16x4 &ident) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const float(&gv)[8] = in.g;
+    const float(&qv)[8] = in.q;
+    const float(&kv)[8] = in.k;
+    // log2 of the cumulative decay: 8 independent prefix sums over the
+    // tokens, written shift-major so that each DPP read finds its source
+    // written several instructions earlier (no hazard stalls)
+    float gam[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gam[j] = gv[j] * kLog2e;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gam[j] += dpp_move<0x111>(gam[j]);  // row_shr:1
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gam[j] += dpp_move<0x112>(gam[j]);  // row_shr:2
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gam[j] += dpp_move<0x114>(gam[j]);  // row_shr:4
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gam[j] += dpp_move<0x118>(gam[j]);  // row_shr:8
+    float ep[8], em[8], eC[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        ep[j] = __builtin_amdgcn_exp2f(gam[j]);
+        em[j] = __builtin_amdgcn_exp2f(-gam[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) eC[j] = row_bcast<15>(ep[j]);  // e^gamma_C of that channel
     float qb[8], kb[8], kh[8], kd[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const float gam = row_prefix_sum(gv[j]);  // gamma of this lane's token, channel of slot j
-        const float ep = __expf(gam);
-        const float em = __builtin_amdgcn_rcpf(ep);
-        ks.eC[j] = row_bcast<15>(ep);             // e^gamma_C of that channel
-        qb[j] = qv[j] * ep;
-        kb[j] = kv[j] * ep;
-        kh[j] = kv[j] * em;
-        kd[j] = kv[j] * (ks.eC[j] * em);
+        qb[j] = qv[j] * ep[j];
+        kb[j] = kv[j] * ep[j];
+        kh[j] = kv[j] * em[j];
+        kd[j] = kh[j] * eC[j];
     }
-    ks.Qb = split8(qb);
-    ks.Kb = split8(kb);
-    const Sp8 Kh = split8(kh), Kd = split8(kd);
-    if (w == 0 && grp == 0) sm.beta[par][n16] = ks.beta;
-
-    // Kd to "channel per lane" for the contraction over tokens
-    ks.KdT[0].hi = transpose_tile(first4(Kd.hi), ident);
-    ks.KdT[0].lo = transpose_tile(first4(Kd.lo), ident);
-    ks.KdT[1].hi = transpose_tile(last4(Kd.hi), ident);
-    ks.KdT[1].lo = transpose_tile(last4(Kd.lo), ident);
-
-    // partial Grams over this wave's 32 channels, transposed:
+    const Sp8 Qb = split8(qb), Kb = split8(kb), Kh = split8(kh), Kd = split8(kd);
+    op.qk[0][kw][0][lane] = Qb.hi;
+    op.qk[0][kw][1][lane] = Qb.lo;
+    op.qk[1][kw][0][lane] = Kb.hi;
+    op.qk[1][kw][1][lane] = Kb.lo;
+    op.kdt[2 * kw][0][lane] = transpose_tile(first4(Kd.hi), ident);
+    op.kdt[2 * kw][1][lane] = transpose_tile(first4(Kd.lo), ident);
+    op.kdt[2 * kw + 1][0][lane] = transpose_tile(last4(Kd.hi), ident);
+    op.kdt[2 * kw + 1][1][lane] = transpose_tile(last4(Kd.lo), ident);
+    if (n16 == 0) {
+        op.eC[8 * kw + grp] = f32x4{eC[0], eC[1], eC[2], eC[3]};
+        op.eC[8 * kw + 4 + grp] = f32x4{eC[4], eC[5], eC[6], eC[7]};
+    }
+    if (kw == 0 && grp == 0) sm.beta[par][n16] = in.beta;
+    // partial Grams over this quarter, transposed:
     // mm32(Kh, Kb)[m][n] = Kh_m . Kb_n = (Kb Kh^T)[n][m], so lane (n, g) gets row n, columns 4g + i
-    sm.gram[par][w][0][n16][grp] = mm32(Kh, ks.Kb, zero);
-    sm.gram[par][w][1][n16][grp] = mm32(Kh, ks.Qb, zero);
+    sm.gram[par][kw][0][lane] = mm32(Kh, Kb, zero);
+    sm.gram[par][kw][1][lane] = mm32(Kh, Qb, zero);
 }
 
-// M = (I + A)^-1 diag(beta) of the chunk with parity `par` (its partial
-// Grams must be visible): wave w solves columns 4w .. 4w + 3, one per 16-lane
-// row.  Returns the P fragment (row n, columns 4g .. 4g + 3).
-__device__ __forceinline__ f32x4 solve(Smem &sm, int par, float beta_r, int w, int grp, int n16) {
+// M = (I + A)^-1 diag(beta) and P of the chunk whose Grams sit in the `par`
+// buffers: wave kw solves columns 4 kw .. 4 kw + 3, one per 16-lane row.
+__device__ __forceinline__ void solve(Smem &sm, int par, int kw, int grp, int n16, int lane) {
     // lane (row r = n, column group g): sum the partial Grams of row r, columns 4g .. 4g + 3
-    f32x4 as = sm.gram[par][0][0][n16][grp], ps = sm.gram[par][0][1][n16][grp];
+    f32x4 as = sm.gram[par][0][0][lane], ps = sm.gram[par][0][1][lane];
 #pragma unroll
     for (int ww = 1; ww < 4; ++ww) {
-        as += sm.gram[par][ww][0][n16][grp];
-        ps += sm.gram[par][ww][1][n16][grp];
+        as += sm.gram[par][ww][0][lane];
+        ps += sm.gram[par][ww][1][lane];
     }
+    const float beta_r = sm.beta[par][n16];
     f32x4 av;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         av[i] = (4 * grp + i < n16) ? beta_r * as[i] : 0.f;
         ps[i] = (4 * grp + i <= n16) ? ps[i] : 0.f;
     }
-    sm.A[w][n16][grp] = av;
+    sm.arow[kw][n16][grp] = av;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     float ar[kC];  // row n of A
 #pragma unroll
     for (int u4 = 0; u4 < 4; ++u4) {
-        const f32x4 row = sm.A[w][n16][u4];
+        const f32x4 row = sm.arow[kw][n16][u4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) ar[4 * u4 + j] = row[j];
     }
-    const int s = 4 * w + grp;  // the column this lane solves
+    const int s = 4 * kw + grp;  // the column this lane solves
     float x = (n16 == s) ? 1.f : 0.f;
     tri_pivots<0>(x, ar);
     sm.M[par][n16][s] = x * sm.beta[par][s];
-    return ps;
+    // every k-side wave forms the same P (same sums in the same order) and
+    // stores it: an unconditional store keeps the solve and the k-side
+    // arithmetic in one basic block
+    *reinterpret_cast<f32x4 *>(&sm.P[par][n16][4 * grp]) = ps;
 }
 
-// Partial X = Kb S0 and Y = Qb S0 over this wave's channels.
-__device__ __forceinline__ void state_xy(Smem &sm, int par, const KSide &ks, const f32x4 (&Sacc)[2][2], int w,
-                                         int grp, int n16) {
+// State part of chunk n (start t0) for state wave (rh, ct): X, Y, U, O and
+// the state update S = diag(e^gamma_C) S0 + Kd^T U of this wave's rows.
+__device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, const Ops &op, int par, int64_t n,
+                                            int64_t t0, const uint16_t (&vr)[4], f32x4 (&S)[4], int64_t b,
+                                            int64_t h, int rh, int ct, int grp, int n16, int lane, int col) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    // operands that do not depend on the state, read first
+    Sp8 Kb[2], Qb[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const float sv[8] = {Sacc[0][c][0], Sacc[0][c][1], Sacc[0][c][2], Sacc[0][c][3],
-                             Sacc[1][c][0], Sacc[1][c][1], Sacc[1][c][2], Sacc[1][c][3]};
+    for (int js = 0; js < 2; ++js) {
+        Kb[js] = Sp8{op.qk[1][2 * rh + js][0][lane], op.qk[1][2 * rh + js][1][lane]};
+        Qb[js] = Sp8{op.qk[0][2 * rh + js][0][lane], op.qk[0][2 * rh + js][1][lane]};
+    }
+    Sp4 KdT[4];
+    f32x4 eC[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        KdT[t] = Sp4{op.kdt[4 * rh + t][0][lane], op.kdt[4 * rh + t][1][lane]};
+        eC[t] = op.eC[16 * rh + 4 * t + grp];
+    }
+    const f32x4 Mrow = *reinterpret_cast<const f32x4 *>(&sm.M[par][n16][4 * grp]);
+
+    // partial X = Kb S0 and Y = Qb S0 over this wave's 64 channels; the state
+    // rows of tiles 2js, 2js + 1 are the channels of operand slots 0..3, 4..7
+    f32x4 X = zero, Y = zero;
+#pragma unroll
+    for (int js = 0; js < 2; ++js) {
+        const float sv[8] = {S[2 * js][0],     S[2 * js][1],     S[2 * js][2],     S[2 * js][3],
+                             S[2 * js + 1][0], S[2 * js + 1][1], S[2 * js + 1][2], S[2 * js + 1][3]};
         const Sp8 Sb = split8(sv);
-        sm.xy[par][w][0][c][n16][grp] = mm32(ks.Kb, Sb, zero);
-        sm.xy[par][w][1][c][n16][grp] = mm32(ks.Qb, Sb, zero);
+        X = mm32(Kb[js], Sb, X);
+        Y = mm32(Qb[js], Sb, Y);
     }
-}
+    sm.xy[rh][0][ct][lane] = X;
+    if (rh == 1) sm.xy[1][1][ct][lane] = Y;
+    // hand the partials to the other row half of this column tile and wait
+    // for its own: its flag reaches n + 1 in this chunk and cannot move
+    // further before the next work-group barrier
+    const uint32_t tag = static_cast<uint32_t>(n + 1);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __hip_atomic_store(&sm.flag[ct][rh], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while (__hip_atomic_load(&sm.flag[ct][rh ^ 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != tag)
+        __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    X += sm.xy[rh ^ 1][0][ct][lane];
 
-// U = M (V - X), O = scale (Y + P U) and S = diag(e^gamma_C) S0 + Kd^T U for
-// the chunk starting at t0 (parity `par`).
-__device__ __forceinline__ void state_update(const PrefillArgs &a, Smem &sm, int par, const KSide &ks,
-                                             const f32x4 &Pfrag, int64_t t0, int64_t b, int64_t h, int col0,
-                                             int w, int grp, int n16, f32x4 (&Sacc)[2][2]) {
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    const int64_t T = a.T, H = a.H;
-    Sp4 Z[2];
+    f32x4 vv;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        f32x4 xs = sm.xy[par][0][0][c][n16][grp];
-#pragma unroll
-        for (int ww = 1; ww < 4; ++ww) xs += sm.xy[par][ww][0][c][n16][grp];
-        Z[c] = split4(ks.v[c] - xs);
-    }
-    const Sp4 Mf = split4(*reinterpret_cast<const f32x4 *>(&sm.M[par][n16][4 * grp]));
-    Sp4 Uc[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) Uc[c] = split4(mm16(Mf, Z[c], zero));
+    for (int i = 0; i < 4; ++i) vv[i] = bf16_bits(vr[i]);
+    const Sp4 U = split4(mm16(split4(Mrow), split4(vv - X), zero));
 
-    // O: waves 0 and 1 write column tiles 0 and 1
-    if (w < 2) {
-        f32x4 Y = sm.xy[par][0][1][w][n16][grp];
-#pragma unroll
-        for (int ww = 1; ww < 4; ++ww) Y += sm.xy[par][ww][1][w][n16][grp];
-        const Sp4 Pf = split4(Pfrag);
-        Sp4 Uw;  // select without a run-time register-array index (which would go to scratch)
-        Uw.hi = (w == 0) ? Uc[0].hi : Uc[1].hi;
-        Uw.lo = (w == 0) ? Uc[0].lo : Uc[1].lo;
-        const f32x4 O = mm16(Pf, Uw, Y);
+    if (rh == 0) {
+        Y += sm.xy[1][1][ct][lane];
+        const f32x4 Prow = *reinterpret_cast<const f32x4 *>(&sm.P[par][n16][4 * grp]);
+        const f32x4 O = mm16(split4(Prow), U, Y);
+        const int64_t T = a.T, H = a.H;
         char *ob = reinterpret_cast<char *>(a.o + ((b * T + t0) * H + h) * kD);  // wave uniform
         const int HD = static_cast<int>(H) * kD;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (t0 + 4 * grp + i < T)
-                *reinterpret_cast<float *>(ob + 4u * static_cast<uint32_t>((4 * grp + i) * HD + col0 + 16 * w + n16)) =
+                *reinterpret_cast<float *>(ob + 4u * static_cast<uint32_t>((4 * grp + i) * HD + col)) =
                     a.scale * O[i];
         }
     }
 
-    // S: the state rows of lane (n, g) are the channels of its operand slots,
-    // so eC[j] is the decay of row 4g + j of tile 0 (j < 4) or of tile 1.
+    // S: lane (n, g) holds rows 4g + i of each tile, the channels of eC[t]
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            f32x4 s0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s0[i] = ks.eC[4 * tt + i] * Sacc[tt][c][i];
-            Sacc[tt][c] = mm16(ks.KdT[tt], Uc[c], s0);
-        }
-    }
+    for (int t = 0; t < 4; ++t) S[t] = mm16(KdT[t], U, eC[t] * S[t]);
 }
 
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     __shared__ Smem sm;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int grp = lane >> 4;
     const int n16 = lane & 15;
@@ -456,75 +481,113 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     const int64_t kk = bid >> 3;
     const int64_t bh = (kk >> 2) * 8 + (bid & 7);
     const int nv = static_cast<int>(kk & 3);
-    if (bh >= BH) return;  // padding blocks of the last XCD round
+    if (bh >= BH) return;  // padding blocks of the last XCD round (whole work-group)
     const int64_t b = bh / a.H, h = bh % a.H;
     const int64_t T = a.T;
+    const int64_t nchunks = (T + kC - 1) / kC;
     const int col0 = nv * kDVS;
-
-    // identity operand for the layout transposes: B[k = 4g + i][col = n] = (4g + i == n)
-    bf16x4 ident;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ident[i] = static_cast<__bf16>((4 * grp + i == n16) ? 1.f : 0.f);
-
-    // State slice rows 16*(2w+tt) + 4*grp + i, columns col0 + 16*c + n16.
-    f32x4 Sacc[2][2];
     const int64_t sbase = bh * kD * kD;
+
+    const bool kwave = w < 4;
+    const int kw = w;              // k-side role: channel quarter
+    const int rh = (w - 4) >> 1;   // state role: row half
+    const int ct = (w - 4) & 1;    //             column tile
+    const int col = col0 + 16 * ct + n16;
+
+    if (tid < 4) (&sm.flag[0][0])[tid] = 0u;
+
+    bf16x4 ident;  // identity operand of the layout transposes: B[k = 4g + i][col = n] = (4g + i == n)
+    KRaw raw[2];
+    f32x4 S[4];  // state rows 64 rh + 16 t + 4 g + i, column `col`
+    uint16_t vraw[2][4];
+    if (kwave) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+        for (int i = 0; i < 4; ++i) ident[i] = static_cast<__bf16>((4 * grp + i == n16) ? 1.f : 0.f);
+        if (nchunks > 0) load_kraw(raw[0], a, 0, b, h, kw, grp, n16);
+        if (nchunks > 1) load_kraw(raw[1], a, kC, b, h, kw, grp, n16);
+    } else {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int t = 0; t < 4; ++t) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = 16 * (2 * w + tt) + 4 * grp + i;
-                Sacc[tt][c][i] = a.h0 ? a.h0[sbase + row * kD + col0 + 16 * c + n16] : 0.f;
+                const int row = 64 * rh + 16 * t + 4 * grp + i;
+                S[t][i] = a.h0 ? a.h0[sbase + row * kD + col] : 0.f;
             }
         }
+        if (nchunks > 0) load_v(vraw[0], a, 0, b, h, col, grp);
+        if (nchunks > 1) load_v(vraw[1], a, kC, b, h, col, grp);
     }
 
-    const int64_t nchunks = (T + kC - 1) / kC;
-    const LaneOffsets off = lane_offsets(a.H, w, grp, n16, col0);
-    if (nchunks > 0) {
-        // Pipeline: iteration n runs the k-side of chunk n + 1 beside the state
-        // contractions of chunk n, then the solve of chunk n + 1 beside the
-        // state update of chunk n; one barrier per chunk.  The loop is unrolled
-        // twice so the per-chunk registers alternate between ks[0] and ks[1]
-        // without copies.
-        RawChunk raw;
-        load_raw(raw, a, 0, b, h, off, grp, n16);
-        KSide ks[2];
-        f32x4 Pf[2];
-        kside(a, sm, raw, 0, nchunks > 1, b, h, off, 0, w, grp, n16, ident, ks[0]);
-        __syncthreads();
-        Pf[0] = solve(sm, 0, ks[0].beta, w, grp, n16);
-        auto step = [&](auto cur_tag, int64_t n) {
-            constexpr int CUR = decltype(cur_tag)::value, NXT = CUR ^ 1;
-            const int64_t t0 = n * kC;
-            const bool has_next = n + 1 < nchunks;
-            state_xy(sm, CUR, ks[CUR], Sacc, w, grp, n16);
-            if (has_next) kside(a, sm, raw, t0 + kC, n + 2 < nchunks, b, h, off, NXT, w, grp, n16, ident, ks[NXT]);
-            __syncthreads();  // X, Y of chunk n, Grams of chunk n + 1 and M of chunk n are in LDS
-            if (has_next) Pf[NXT] = solve(sm, NXT, ks[NXT].beta, w, grp, n16);
-            state_update(a, sm, CUR, ks[CUR], Pf[CUR], t0, b, h, col0, w, grp, n16, Sacc);
-            // No second barrier: xy[CUR] and gram[NXT] are rewritten only after
-            // the next barrier, and M[NXT], written above, is read only after it.
-        };
-        for (int64_t n = 0; n < nchunks; n += 2) {
-            step(std::integral_constant<int, 0>{}, n);
-            if (n + 1 >= nchunks) break;
-            step(std::integral_constant<int, 1>{}, n + 1);
+    // Step n: the k-side waves solve chunk n + 1 and prepare chunk n + 2
+    // while the state waves run chunk n; one barrier ends the step.  Steps
+    // n = -2, -1 fill the pipeline, the last two drain it; in between every
+    // step does all three parts with no run-time tests, so the solve's
+    // latency chain and the k-side's vector work share one instruction
+    // stream.  Parity and phase are template arguments, so the register
+    // double-buffers (raw inputs, values) are indexed statically.  Prefetches
+    // past the last chunk are clamped to it (harmless re-reads).
+    const int64_t last_t0 = nchunks > 0 ? (nchunks - 1) * kC : 0;
+    int kslot = 0, sslot = 1;  // ring slots of chunks n + 2 and n, for n = -2
+    auto step = [&](auto par_tag, auto solve_tag, auto kside_tag, auto state_tag, int64_t n) {
+        constexpr int PAR = decltype(par_tag)::value;  // n & 1
+        if (kwave) {
+            // unpack and reload first, so that the solve and the k-side
+            // arithmetic sit in one basic block
+            KIn in;
+            if constexpr (decltype(kside_tag)::value)
+                kside_in(a, raw[PAR], in, (n + 2) * kC, min((n + 4) * kC, last_t0), b, h, kw, grp, n16);
+            if constexpr (decltype(solve_tag)::value) solve(sm, PAR ^ 1, kw, grp, n16, lane);
+            if constexpr (decltype(kside_tag)::value) kside(sm, sm.ops[kslot], in, PAR, kw, grp, n16, lane, ident);
+        } else {
+            if constexpr (decltype(state_tag)::value) {
+                state_chunk(a, sm, sm.ops[sslot], PAR, n, n * kC, vraw[PAR], S, b, h, rh, ct, grp, n16, lane, col);
+                load_v(vraw[PAR], a, min((n + 2) * kC, last_t0), b, h, col, grp);
+            }
         }
+        kslot = (kslot == kRing - 1) ? 0 : kslot + 1;
+        sslot = (sslot == kRing - 1) ? 0 : sslot + 1;
+        __syncthreads();
+    };
+    using F = std::false_type;
+    using Tr = std::true_type;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    if (nchunks > 0) {
+        step(P0{}, F{}, Tr{}, F{}, -2);  // k-side of chunk 0
+        if (nchunks > 1)
+            step(P1{}, Tr{}, Tr{}, F{}, -1);  // solve 0, k-side of chunk 1
+        else
+            step(P1{}, Tr{}, F{}, F{}, -1);
+        int64_t n = 0;
+        for (; n + 1 < nchunks - 2; n += 2) {  // steady state: chunks n + 2, n + 3 exist
+            step(P0{}, Tr{}, Tr{}, Tr{}, n);
+            step(P1{}, Tr{}, Tr{}, Tr{}, n + 1);
+        }
+        if (n < nchunks - 2) {
+            step(P0{}, Tr{}, Tr{}, Tr{}, n);
+            ++n;
+        }
+        // drain: step N - 2 (solve of the last chunk) and step N - 1
+        if (n == nchunks - 2) {
+            if (n & 1)
+                step(P1{}, Tr{}, F{}, Tr{}, n);
+            else
+                step(P0{}, Tr{}, F{}, Tr{}, n);
+            ++n;
+        }
+        if (n & 1)
+            step(P1{}, F{}, F{}, Tr{}, n);
+        else
+            step(P0{}, F{}, F{}, Tr{}, n);
     }
 
-    if (a.hT) {
+    if (!kwave && a.hT) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int t = 0; t < 4; ++t) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * (2 * w + tt) + 4 * grp + i;
-                    a.hT[sbase + row * kD + col0 + 16 * c + n16] = Sacc[tt][c][i];
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int row = 64 * rh + 16 * t + 4 * grp + i;
+                a.hT[sbase + row * kD + col] = S[t][i];
             }
         }
     }
@@ -533,7 +596,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
 }  // namespace
 
 bool prefill_mfma_supported(const PrefillArgs &a) {
-    if (a.D != kD || !a.bf16) return false;
+    // the kernel's 32-bit in-chunk byte offsets need 16 * H * 128 * 4 < 2^31
+    if (a.D != kD || !a.bf16 || a.H > 65536) return false;
     const char *env = getenv("KDA_DISABLE_MFMA");
     return !(env && env[0] == '1');
 }
@@ -541,7 +605,7 @@ bool prefill_mfma_supported(const PrefillArgs &a) {
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
     const int64_t BH = a.B * a.H;
     const int64_t rounds = (BH + 7) / 8;
-    dim3 grid(static_cast<unsigned>(rounds * 8 * kNV)), block(256);
+    dim3 grid(static_cast<unsigned>(rounds * 8 * kNV)), block(kThreads);
     hipLaunchKernelGGL(prefill_mfma_kernel, grid, block, 0, s, a);
     return hipGetLastError();
 }
