@@ -10,14 +10,17 @@
 // per-channel cumulative log-decay gamma_r = g_1 + ... + g_r and
 // gamma_C = gamma_16:
 //   Qb = q * e^gamma      Kb = k * e^gamma      Kh = k * e^-gamma
-//   Kd = k * e^(gamma_C - gamma)
 //   A  = strict_lower(diag(beta) Kb Kh^T)        (I + A) is unit lower triangular
 //   P  = lower(Qb Kh^T)
 //   M  = (I + A)^-1 diag(beta)
 //   X  = Kb S0,   Y = Qb S0                      (the two state contractions)
 //   U  = M (V - X)
 //   O  = scale * (Y + P U)
-//   S  = diag(e^gamma_C) S0 + Kd^T U
+//   S  = diag(e^gamma_C) (S0 + Kh^T U)
+// The last line is diag(e^gamma_C) S0 + Kd^T U with Kd = k * e^(gamma_C - gamma)
+// written with the per-channel factor e^gamma_C taken out of Kd, so the
+// update needs no operand of its own: the channel sum S0 + Kh^T U is formed
+// in fp32 and then scaled, which keeps both terms' relative accuracy.
 // The 16-token chunk with gates >= -5 keeps every e^(+-gamma) inside the bf16
 // normal range, so all products can use bf16 matrix instructions (Kimi K3
 // paper digest, devpress.csdn.net, section 2.1 (1)).  Each product is taken
@@ -50,9 +53,9 @@
 // result layout of 16-row tiles, which lists the same channels in the same
 // slots.  q, k, g are loaded straight into it with 8- and 16-byte loads, and
 // the cumulative decay over tokens is a prefix sum across the 16 lanes of a
-// row (DPP row shifts).  Kd, the operand of the contraction over tokens,
-// needs "channel per lane" (channel n, tokens 4g .. 4g + 3): a 16x16x16
-// product with the identity converts it exactly (its inputs are bf16).  The
+// row (DPP row shifts).  Kh in the update, a contraction over tokens, needs
+// "channel per lane" (channel n, tokens 4g .. 4g + 3): a 16x16x16 product
+// with the identity converts it exactly (its inputs are bf16).  The
 // Grams are formed transposed (Kh Kb^T, Kh Qb^T), so their result layout is
 // "row n, columns 4g + i", the A-operand layout of U = M Z and P U.
 #include <type_traits>
@@ -196,7 +199,7 @@ __device__ __forceinline__ void tri_pivots(float &x, const float (&ar)[kC]) {
 // (every access is lane-contiguous).
 struct Ops {
     bf16x8 qk[2][4][2][64];  // [Qb, Kb][32-channel quarter][hi, lo][lane], token per lane
-    bf16x4 kdt[8][2][64];    // [16-channel tile][hi, lo][lane], Kd channel per lane
+    bf16x4 kht[8][2][64];    // [16-channel tile][hi, lo][lane], Kh channel per lane
     f32x4 eC[kD / 4];        // e^gamma_C of channels 4i .. 4i + 3
 };
 
@@ -204,7 +207,7 @@ struct Smem {
     Ops ops[kRing];
     f32x4 gram[2][4][2][64];      // partial Grams [parity][k-side wave][A, P][lane]
     f32x4 arow[4][kC][5];         // summed, masked A per k-side wave; rows padded to 80 bytes
-    alignas(16) float M[2][kC][20];  // M = (I + A)^-1 diag(beta) [parity][row][column], padded rows
+    bf16x4 Mhl[2][2][64];         // M = (I + A)^-1 diag(beta), split [parity][hi, lo][lane], A-operand layout
     alignas(16) float P[2][kC][20];  // P [parity][row][column], padded rows
     float beta[2][kC];
     f32x4 xy[2][2][2][64];        // partial X, Y [row half][X, Y][column tile][lane]
@@ -221,16 +224,25 @@ struct KRaw {
 };
 
 // Loads never branch per element and never leave the sequence: in a last,
-// partial chunk the token index is clamped.  Offsets are unsigned 32-bit byte
-// offsets (16 tokens of a row of H heads stay below 2^31 bytes for the head
-// counts this kernel accepts) added to a wave-uniform 64-bit base.
+// partial chunk the token index is clamped.  Offsets are unsigned 32-bit
+// element offsets (16 tokens of a row of H heads stay below 2^31 bytes for
+// the head counts this kernel accepts) added to a wave-uniform 64-bit base;
+// the offsets of full chunks are loop invariants computed once.
+struct KOff {
+    uint32_t tok;   // token n, channel 32 kw + 4 g (elements)
+    uint32_t beta;  // token n (elements of beta)
+};
+__device__ __forceinline__ KOff kraw_offsets(const PrefillArgs &a, int tok, int kw, int grp) {
+    const int HD = static_cast<int>(a.H) * kD;
+    return KOff{static_cast<uint32_t>(tok * HD + 32 * kw + 4 * grp), static_cast<uint32_t>(tok * static_cast<int>(a.H))};
+}
 __device__ __forceinline__ void load_kraw(KRaw &r, const PrefillArgs &a, int64_t t0, int64_t b, int64_t h, int kw,
-                                          int grp, int n16) {
+                                          int grp, int n16, const KOff &full) {
     const int64_t T = a.T, H = a.H;
     const int64_t row0 = (b * T + t0) * H + h;  // token row of the chunk start (wave uniform)
-    const int HD = static_cast<int>(H) * kD;
-    const int tok = (t0 + kC <= T) ? n16 : min(n16, static_cast<int>(T - t0) - 1);
-    const uint32_t e0 = static_cast<uint32_t>(tok * HD + 32 * kw + 4 * grp);
+    KOff off = full;
+    if (t0 + kC > T) off = kraw_offsets(a, min(n16, static_cast<int>(T - t0) - 1), kw, grp);
+    const uint32_t e0 = off.tok;
     const char *gb = reinterpret_cast<const char *>(a.g + row0 * kD);
     const char *qb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.q) + row0 * kD);
     const char *kb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k) + row0 * kD);
@@ -241,23 +253,25 @@ __device__ __forceinline__ void load_kraw(KRaw &r, const PrefillArgs &a, int64_t
         r.k[tt] = *reinterpret_cast<const u32x2 *>(kb + 2u * e);
         r.g[tt] = *reinterpret_cast<const f32x4 *>(gb + 4u * e);
     }
-    r.beta = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(a.beta + row0) +
-                                              4u * static_cast<uint32_t>(tok * static_cast<int>(H)));
+    r.beta = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(a.beta + row0) + 4u * off.beta);
 }
 
-// Values of one chunk for a state lane: token 4g + i, value column `col`.
+// Values of one chunk for a state lane: token 4g + i, value column `col`;
+// `full` holds the element offsets of a full chunk.
 __device__ __forceinline__ void load_v(uint16_t (&v)[4], const PrefillArgs &a, int64_t t0, int64_t b, int64_t h,
-                                       int col, int grp) {
+                                       int col, int grp, const uint32_t (&full)[4]) {
     const int64_t T = a.T, H = a.H;
     const int64_t row0 = (b * T + t0) * H + h;
     const char *vb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.v) + row0 * kD);
     const int HD = static_cast<int>(H) * kD;
-    const int last = (t0 + kC <= T) ? kC - 1 : static_cast<int>(T - t0) - 1;
+    uint32_t off[4] = {full[0], full[1], full[2], full[3]};
+    if (t0 + kC > T) {
+        const int last = static_cast<int>(T - t0) - 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int tok = min(4 * grp + i, last);
-        v[i] = *reinterpret_cast<const uint16_t *>(vb + 2u * static_cast<uint32_t>(tok * HD + col));
+        for (int i = 0; i < 4; ++i) off[i] = static_cast<uint32_t>(min(4 * grp + i, last) * HD + col);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const uint16_t *>(vb + 2u * off[i]);
 }
 
 // Unpacked inputs of one chunk for a k-side lane (channel slot j of token n).
@@ -267,13 +281,12 @@ struct KIn {
 };
 
 // K-side, first part, for the chunk starting at t0: unpacks the raw inputs in
-// `raw` and then issues the loads of the chunk starting at t_next into the
-// same registers.
+// `raw` (the caller reloads `raw` once the unpacked values are dead, so that
+// no loaded register is copied and no wait covers a younger load).
 // Tokens past the end of the sequence become identity steps: their gate is
 // set to 0 and their beta to 0.  That zeroes their rows and columns of A and
 // M, hence their rows of U, so their (finite) q, k and v never contribute.
-__device__ __forceinline__ void kside_in(const PrefillArgs &a, KRaw &raw, KIn &in, int64_t t0, int64_t t_next,
-                                         int64_t b, int64_t h, int kw, int grp, int n16) {
+__device__ __forceinline__ void kside_in(const PrefillArgs &a, const KRaw &raw, KIn &in, int64_t t0, int n16) {
     in.beta = raw.beta;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -295,7 +308,6 @@ __device__ __forceinline__ void kside_in(const PrefillArgs &a, KRaw &raw, KIn &i
             in.beta = 0.f;
         }
     }
-    load_kraw(raw, a, t_next, b, h, kw, grp, n16);
 }
 
 // K-side, second part: this quarter's operands of the chunk go to `op`, its
@@ -328,23 +340,22 @@ __device__ __forceinline__ void kside(Smem &sm, Ops &op, const KIn &in, int par,
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) eC[j] = row_bcast<15>(ep[j]);  // e^gamma_C of that channel
-    float qb[8], kb[8], kh[8], kd[8];
+    float qb[8], kb[8], kh[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         qb[j] = qv[j] * ep[j];
         kb[j] = kv[j] * ep[j];
         kh[j] = kv[j] * em[j];
-        kd[j] = kh[j] * eC[j];
     }
-    const Sp8 Qb = split8(qb), Kb = split8(kb), Kh = split8(kh), Kd = split8(kd);
+    const Sp8 Qb = split8(qb), Kb = split8(kb), Kh = split8(kh);
     op.qk[0][kw][0][lane] = Qb.hi;
     op.qk[0][kw][1][lane] = Qb.lo;
     op.qk[1][kw][0][lane] = Kb.hi;
     op.qk[1][kw][1][lane] = Kb.lo;
-    op.kdt[2 * kw][0][lane] = transpose_tile(first4(Kd.hi), ident);
-    op.kdt[2 * kw][1][lane] = transpose_tile(first4(Kd.lo), ident);
-    op.kdt[2 * kw + 1][0][lane] = transpose_tile(last4(Kd.hi), ident);
-    op.kdt[2 * kw + 1][1][lane] = transpose_tile(last4(Kd.lo), ident);
+    op.kht[2 * kw][0][lane] = transpose_tile(first4(Kh.hi), ident);
+    op.kht[2 * kw][1][lane] = transpose_tile(first4(Kh.lo), ident);
+    op.kht[2 * kw + 1][0][lane] = transpose_tile(last4(Kh.hi), ident);
+    op.kht[2 * kw + 1][1][lane] = transpose_tile(last4(Kh.lo), ident);
     if (n16 == 0) {
         op.eC[8 * kw + grp] = f32x4{eC[0], eC[1], eC[2], eC[3]};
         op.eC[8 * kw + 4 + grp] = f32x4{eC[4], eC[5], eC[6], eC[7]};
@@ -387,7 +398,13 @@ __device__ __forceinline__ void solve(Smem &sm, int par, int kw, int grp, int n1
     const int s = 4 * kw + grp;  // the column this lane solves
     float x = (n16 == s) ? 1.f : 0.f;
     tri_pivots<0>(x, ar);
-    sm.M[par][n16][s] = x * sm.beta[par][s];
+    // M[n][s] goes to slot s % 4 = grp of lane 16 (s / 4) + n = 16 kw + n of
+    // the A operand of U = M Z, as a hi/lo bf16 pair
+    const float m = x * sm.beta[par][s];
+    const __bf16 mh = static_cast<__bf16>(m);
+    const __bf16 ml = static_cast<__bf16>(m - static_cast<float>(mh));
+    reinterpret_cast<__bf16 *>(&sm.Mhl[par][0][16 * kw + n16])[grp] = mh;
+    reinterpret_cast<__bf16 *>(&sm.Mhl[par][1][16 * kw + n16])[grp] = ml;
     // every k-side wave forms the same P (same sums in the same order) and
     // stores it: an unconditional store keeps the solve and the k-side
     // arithmetic in one basic block
@@ -395,7 +412,7 @@ __device__ __forceinline__ void solve(Smem &sm, int par, int kw, int grp, int n1
 }
 
 // State part of chunk n (start t0) for state wave (rh, ct): X, Y, U, O and
-// the state update S = diag(e^gamma_C) S0 + Kd^T U of this wave's rows.
+// the state update S = diag(e^gamma_C) (S0 + Kh^T U) of this wave's rows.
 __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, const Ops &op, int par, int64_t n,
                                             int64_t t0, const uint16_t (&vr)[4], f32x4 (&S)[4], int64_t b,
                                             int64_t h, int rh, int ct, int grp, int n16, int lane, int col) {
@@ -407,14 +424,14 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
         Kb[js] = Sp8{op.qk[1][2 * rh + js][0][lane], op.qk[1][2 * rh + js][1][lane]};
         Qb[js] = Sp8{op.qk[0][2 * rh + js][0][lane], op.qk[0][2 * rh + js][1][lane]};
     }
-    Sp4 KdT[4];
+    Sp4 KhT[4];
     f32x4 eC[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        KdT[t] = Sp4{op.kdt[4 * rh + t][0][lane], op.kdt[4 * rh + t][1][lane]};
+        KhT[t] = Sp4{op.kht[4 * rh + t][0][lane], op.kht[4 * rh + t][1][lane]};
         eC[t] = op.eC[16 * rh + 4 * t + grp];
     }
-    const f32x4 Mrow = *reinterpret_cast<const f32x4 *>(&sm.M[par][n16][4 * grp]);
+    const Sp4 Mf = Sp4{sm.Mhl[par][0][lane], sm.Mhl[par][1][lane]};
 
     // partial X = Kb S0 and Y = Qb S0 over this wave's 64 channels; the state
     // rows of tiles 2js, 2js + 1 are the channels of operand slots 0..3, 4..7
@@ -443,7 +460,7 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
     f32x4 vv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) vv[i] = bf16_bits(vr[i]);
-    const Sp4 U = split4(mm16(split4(Mrow), split4(vv - X), zero));
+    const Sp4 U = split4(mm16(Mf, split4(vv - X), zero));
 
     if (rh == 0) {
         Y += sm.xy[1][1][ct][lane];
@@ -462,7 +479,55 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
 
     // S: lane (n, g) holds rows 4g + i of each tile, the channels of eC[t]
 #pragma unroll
-    for (int t = 0; t < 4; ++t) S[t] = mm16(KdT[t], U, eC[t] * S[t]);
+    for (int t = 0; t < 4; ++t) S[t] = eC[t] * mm16(KhT[t], U, S[t]);
+}
+
+// The step sequence of a work-group over nchunks chunks, with one barrier
+// after each step.  Step n runs body(parity, solve, kside, state, n), where
+// the three flags (compile-time) say whether chunk n + 1 is solved, chunk
+// n + 2 prepared and chunk n advanced: steps -2 and -1 fill the pipeline,
+// the last two drain it, and every step in between does all three.  Both
+// roles call this with the same nchunks, so they meet the same barriers.
+template <class Body>
+__device__ __forceinline__ void run_steps(int64_t nchunks, Body &&body) {
+    using F = std::false_type;
+    using Tr = std::true_type;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    if (nchunks <= 0) return;
+    // steps -2 and -1 always run the k-side (with one chunk, step -1 prepares
+    // a chunk past the end whose tokens are all masked and whose operands
+    // are never read): the same load pattern on every path keeps the
+    // compiler's load-count bookkeeping exact at the loop entry
+    body(P0{}, F{}, Tr{}, F{}, -2);  // k-side of chunk 0
+    __syncthreads();
+    body(P1{}, Tr{}, Tr{}, F{}, -1);  // solve of chunk 0, k-side of chunk 1
+    __syncthreads();
+    int64_t n = 0;
+    for (; n + 1 < nchunks - 2; n += 2) {  // chunks n + 2 and n + 3 exist
+        body(P0{}, Tr{}, Tr{}, Tr{}, n);
+        __syncthreads();
+        body(P1{}, Tr{}, Tr{}, Tr{}, n + 1);
+        __syncthreads();
+    }
+    if (n < nchunks - 2) {
+        body(P0{}, Tr{}, Tr{}, Tr{}, n);
+        __syncthreads();
+        ++n;
+    }
+    if (n == nchunks - 2) {  // solve of the last chunk
+        if (n & 1)
+            body(P1{}, Tr{}, F{}, Tr{}, n);
+        else
+            body(P0{}, Tr{}, F{}, Tr{}, n);
+        __syncthreads();
+        ++n;
+    }
+    if (n & 1)
+        body(P1{}, F{}, F{}, Tr{}, n);
+    else
+        body(P0{}, F{}, F{}, Tr{}, n);
+    __syncthreads();
 }
 
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
@@ -497,14 +562,20 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     if (tid < 4) (&sm.flag[0][0])[tid] = 0u;
 
     bf16x4 ident;  // identity operand of the layout transposes: B[k = 4g + i][col = n] = (4g + i == n)
+    const KOff koff = kraw_offsets(a, n16, kw, grp);
+    uint32_t voff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) voff[i] = static_cast<uint32_t>((4 * grp + i) * static_cast<int>(a.H) * kD + col);
     KRaw raw[2];
     f32x4 S[4];  // state rows 64 rh + 16 t + 4 g + i, column `col`
     uint16_t vraw[2][4];
     if (kwave) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) ident[i] = static_cast<__bf16>((4 * grp + i == n16) ? 1.f : 0.f);
-        if (nchunks > 0) load_kraw(raw[0], a, 0, b, h, kw, grp, n16);
-        if (nchunks > 1) load_kraw(raw[1], a, kC, b, h, kw, grp, n16);
+        if (nchunks > 0) {
+            load_kraw(raw[0], a, 0, b, h, kw, grp, n16, koff);
+            load_kraw(raw[1], a, nchunks > 1 ? kC : 0, b, h, kw, grp, n16, koff);
+        }
     } else {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -514,71 +585,43 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
                 S[t][i] = a.h0 ? a.h0[sbase + row * kD + col] : 0.f;
             }
         }
-        if (nchunks > 0) load_v(vraw[0], a, 0, b, h, col, grp);
-        if (nchunks > 1) load_v(vraw[1], a, kC, b, h, col, grp);
+        if (nchunks > 0) {
+            load_v(vraw[0], a, 0, b, h, col, grp, voff);
+            load_v(vraw[1], a, nchunks > 1 ? kC : 0, b, h, col, grp, voff);
+        }
     }
 
     // Step n: the k-side waves solve chunk n + 1 and prepare chunk n + 2
-    // while the state waves run chunk n; one barrier ends the step.  Steps
-    // n = -2, -1 fill the pipeline, the last two drain it; in between every
-    // step does all three parts with no run-time tests, so the solve's
-    // latency chain and the k-side's vector work share one instruction
-    // stream.  Parity and phase are template arguments, so the register
-    // double-buffers (raw inputs, values) are indexed statically.  Prefetches
-    // past the last chunk are clamped to it (harmless re-reads).
+    // while the state waves run chunk n; one barrier ends the step.  Each
+    // role runs its own copy of the step sequence (see run_steps), so the
+    // register double-buffers of one role never meet the other's in a loop
+    // phi, and loaded values are consumed in the registers they land in.
     const int64_t last_t0 = nchunks > 0 ? (nchunks - 1) * kC : 0;
-    int kslot = 0, sslot = 1;  // ring slots of chunks n + 2 and n, for n = -2
-    auto step = [&](auto par_tag, auto solve_tag, auto kside_tag, auto state_tag, int64_t n) {
-        constexpr int PAR = decltype(par_tag)::value;  // n & 1
-        if (kwave) {
-            // unpack and reload first, so that the solve and the k-side
-            // arithmetic sit in one basic block
+    if (kwave) {
+        int kslot = 0;  // ring slot of chunk n + 2
+        run_steps(nchunks, [&](auto par_tag, auto solve_tag, auto kside_tag, auto, int64_t n) {
+            constexpr int PAR = decltype(par_tag)::value;  // n & 1
+            // unpack first, so that the solve and the k-side arithmetic sit
+            // in one basic block; reload the raw buffer at the end
             KIn in;
-            if constexpr (decltype(kside_tag)::value)
-                kside_in(a, raw[PAR], in, (n + 2) * kC, min((n + 4) * kC, last_t0), b, h, kw, grp, n16);
+            if constexpr (decltype(kside_tag)::value) kside_in(a, raw[PAR], in, (n + 2) * kC, n16);
             if constexpr (decltype(solve_tag)::value) solve(sm, PAR ^ 1, kw, grp, n16, lane);
-            if constexpr (decltype(kside_tag)::value) kside(sm, sm.ops[kslot], in, PAR, kw, grp, n16, lane, ident);
-        } else {
+            if constexpr (decltype(kside_tag)::value) {
+                kside(sm, sm.ops[kslot], in, PAR, kw, grp, n16, lane, ident);
+                load_kraw(raw[PAR], a, min((n + 4) * kC, last_t0), b, h, kw, grp, n16, koff);
+            }
+            kslot = (kslot == kRing - 1) ? 0 : kslot + 1;
+        });
+    } else {
+        int sslot = 1;  // ring slot of chunk n (n = -2 maps to slot 1)
+        run_steps(nchunks, [&](auto par_tag, auto, auto, auto state_tag, int64_t n) {
+            constexpr int PAR = decltype(par_tag)::value;
             if constexpr (decltype(state_tag)::value) {
                 state_chunk(a, sm, sm.ops[sslot], PAR, n, n * kC, vraw[PAR], S, b, h, rh, ct, grp, n16, lane, col);
-                load_v(vraw[PAR], a, min((n + 2) * kC, last_t0), b, h, col, grp);
+                load_v(vraw[PAR], a, min((n + 2) * kC, last_t0), b, h, col, grp, voff);
             }
-        }
-        kslot = (kslot == kRing - 1) ? 0 : kslot + 1;
-        sslot = (sslot == kRing - 1) ? 0 : sslot + 1;
-        __syncthreads();
-    };
-    using F = std::false_type;
-    using Tr = std::true_type;
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
-    if (nchunks > 0) {
-        step(P0{}, F{}, Tr{}, F{}, -2);  // k-side of chunk 0
-        if (nchunks > 1)
-            step(P1{}, Tr{}, Tr{}, F{}, -1);  // solve 0, k-side of chunk 1
-        else
-            step(P1{}, Tr{}, F{}, F{}, -1);
-        int64_t n = 0;
-        for (; n + 1 < nchunks - 2; n += 2) {  // steady state: chunks n + 2, n + 3 exist
-            step(P0{}, Tr{}, Tr{}, Tr{}, n);
-            step(P1{}, Tr{}, Tr{}, Tr{}, n + 1);
-        }
-        if (n < nchunks - 2) {
-            step(P0{}, Tr{}, Tr{}, Tr{}, n);
-            ++n;
-        }
-        // drain: step N - 2 (solve of the last chunk) and step N - 1
-        if (n == nchunks - 2) {
-            if (n & 1)
-                step(P1{}, Tr{}, F{}, Tr{}, n);
-            else
-                step(P0{}, Tr{}, F{}, Tr{}, n);
-            ++n;
-        }
-        if (n & 1)
-            step(P1{}, F{}, F{}, Tr{}, n);
-        else
-            step(P0{}, F{}, F{}, Tr{}, n);
+            sslot = (sslot == kRing - 1) ? 0 : sslot + 1;
+        });
     }
 
     if (!kwave && a.hT) {
