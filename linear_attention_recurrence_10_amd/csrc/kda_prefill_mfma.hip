@@ -27,20 +27,21 @@
 // in three bf16 passes (x = x_hi + x_lo; a*b ~ a_hi b_hi + a_hi b_lo +
 // a_lo b_hi) with fp32 accumulation, which keeps fp32-level accuracy.
 //
-// Work split inside a work-group: 8 waves, two per SIMD, in two roles.
+// Work split inside a work-group: 12 waves, three per SIMD, in three roles.
 //  * k-side waves 0..3 work ahead of the state: wave kw takes key channels
 //    [32 kw, 32 kw + 32) of chunk n + 2 (gate prefix sums, exponentials, the
-//    scaled and split operands, its partial Grams) and solves M of chunk n + 1.
-//    Everything they produce goes to LDS: a ring of three chunks of operands,
-//    double-buffered Grams, M and P.
+//    scaled and split operands, its partial Grams).  Everything they produce
+//    goes to LDS: a ring of three chunks of operands, double-buffered Grams.
+//  * solver waves 8..11 sum the partial Grams of chunk n + 1 and solve
+//    (I + A) M = diag(beta), four columns each, and form P (double-buffered).
 //  * state waves 4..7 carry the state slice: wave (row half rh, column tile
 //    ct) holds state rows [64 rh, 64 rh + 64) x columns 16 ct .. 16 ct + 15
 //    in registers and runs the state part of chunk n.  The two row halves of
 //    a column tile exchange their partial X, Y through LDS with a flag
 //    handshake; both then form the same U for their own rows.
 // One work-group barrier per chunk hands the k-side of later chunks to the
-// state waves; a k-side wave and a state wave share each SIMD, so one's
-// vector work fills the other's matrix-core and LDS latency.
+// state waves; one wave of each role shares each SIMD, so one's vector work
+// fills the others' matrix-core, LDS and dependency latency.
 //
 // Operand layouts (lane l, row group g = l / 16, n = l % 16):
 //   16x16x16 (bf16_1k):  A[m = n][k = 4g + i],  B[k = 4g + i][col = n]
@@ -78,7 +79,7 @@ constexpr int kD = 128;     // head dimension (d_k = d_v)
 constexpr int kDVS = 32;    // value columns per work-group
 constexpr int kNV = kD / kDVS;
 constexpr int kC = kChunk;  // 16
-constexpr int kThreads = 512;
+constexpr int kThreads = 768;
 constexpr int kRing = 3;    // chunks of k-side operands in flight
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -206,7 +207,7 @@ struct Ops {
 struct Smem {
     Ops ops[kRing];
     f32x4 gram[2][4][2][64];      // partial Grams [parity][k-side wave][A, P][lane]
-    f32x4 arow[4][kC][5];         // summed, masked A per k-side wave; rows padded to 80 bytes
+    f32x4 arow[4][kC][5];         // summed, masked A per solver wave; rows padded to 80 bytes
     bf16x4 Mhl[2][2][64];         // M = (I + A)^-1 diag(beta), split [parity][hi, lo][lane], A-operand layout
     alignas(16) float P[2][kC][20];  // P [parity][row][column], padded rows
     float beta[2][kC];
@@ -368,7 +369,7 @@ __device__ __forceinline__ void kside(Smem &sm, Ops &op, const KIn &in, int par,
 }
 
 // M = (I + A)^-1 diag(beta) and P of the chunk whose Grams sit in the `par`
-// buffers: wave kw solves columns 4 kw .. 4 kw + 3, one per 16-lane row.
+// buffers: solver wave kw solves columns 4 kw .. 4 kw + 3, one per 16-lane row.
 __device__ __forceinline__ void solve(Smem &sm, int par, int kw, int grp, int n16, int lane) {
     // lane (row r = n, column group g): sum the partial Grams of row r, columns 4g .. 4g + 3
     f32x4 as = sm.gram[par][0][0][lane], ps = sm.gram[par][0][1][lane];
@@ -405,9 +406,8 @@ __device__ __forceinline__ void solve(Smem &sm, int par, int kw, int grp, int n1
     const __bf16 ml = static_cast<__bf16>(m - static_cast<float>(mh));
     reinterpret_cast<__bf16 *>(&sm.Mhl[par][0][16 * kw + n16])[grp] = mh;
     reinterpret_cast<__bf16 *>(&sm.Mhl[par][1][16 * kw + n16])[grp] = ml;
-    // every k-side wave forms the same P (same sums in the same order) and
-    // stores it: an unconditional store keeps the solve and the k-side
-    // arithmetic in one basic block
+    // every solver wave forms the same P (same sums in the same order) and
+    // stores it (no branch on the wave index)
     *reinterpret_cast<f32x4 *>(&sm.P[par][n16][4 * grp]) = ps;
 }
 
@@ -554,9 +554,11 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     const int64_t sbase = bh * kD * kD;
 
     const bool kwave = w < 4;
+    const bool swave = w >= 4 && w < 8;
     const int kw = w;              // k-side role: channel quarter
     const int rh = (w - 4) >> 1;   // state role: row half
     const int ct = (w - 4) & 1;    //             column tile
+    const int sv = w - 8;          // solver role: columns 4 sv .. 4 sv + 3
     const int col = col0 + 16 * ct + n16;
 
     if (tid < 4) (&sm.flag[0][0])[tid] = 0u;
@@ -576,7 +578,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             load_kraw(raw[0], a, 0, b, h, kw, grp, n16, koff);
             load_kraw(raw[1], a, nchunks > 1 ? kC : 0, b, h, kw, grp, n16, koff);
         }
-    } else {
+    } else if (swave) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -599,18 +601,21 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     const int64_t last_t0 = nchunks > 0 ? (nchunks - 1) * kC : 0;
     if (kwave) {
         int kslot = 0;  // ring slot of chunk n + 2
-        run_steps(nchunks, [&](auto par_tag, auto solve_tag, auto kside_tag, auto, int64_t n) {
+        run_steps(nchunks, [&](auto par_tag, auto, auto kside_tag, auto, int64_t n) {
             constexpr int PAR = decltype(par_tag)::value;  // n & 1
-            // unpack first, so that the solve and the k-side arithmetic sit
-            // in one basic block; reload the raw buffer at the end
+            // reload the raw buffer at the end, once the unpacked values are dead
             KIn in;
             if constexpr (decltype(kside_tag)::value) kside_in(a, raw[PAR], in, (n + 2) * kC, n16);
-            if constexpr (decltype(solve_tag)::value) solve(sm, PAR ^ 1, kw, grp, n16, lane);
             if constexpr (decltype(kside_tag)::value) {
                 kside(sm, sm.ops[kslot], in, PAR, kw, grp, n16, lane, ident);
                 load_kraw(raw[PAR], a, min((n + 4) * kC, last_t0), b, h, kw, grp, n16, koff);
             }
             kslot = (kslot == kRing - 1) ? 0 : kslot + 1;
+        });
+    } else if (!swave) {
+        run_steps(nchunks, [&](auto par_tag, auto solve_tag, auto, auto, int64_t) {
+            constexpr int PAR = decltype(par_tag)::value;  // n & 1
+            if constexpr (decltype(solve_tag)::value) solve(sm, PAR ^ 1, sv, grp, n16, lane);
         });
     } else {
         int sslot = 1;  // ring slot of chunk n (n = -2 maps to slot 1)
@@ -624,7 +629,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
         });
     }
 
-    if (!kwave && a.hT) {
+    if (swave && a.hT) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
 #pragma unroll
