@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--ckpt-every", type=int, default=0,
+                    help="also time the prefill that writes state checkpoints every N tokens (N a multiple of 16)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain device copy of %d bytes first (for the traffic counters)" % (1 << 30))
     args = ap.parse_args()
@@ -197,6 +199,21 @@ def main():
             decode(dec_ev[i])
     torch.cuda.synchronize()
     wall_dec = time.perf_counter() - t0
+    ck_ms = []
+    if args.ckpt_every > 0:
+        n_ck = cfg.T // args.ckpt_every
+        ck = torch.empty((n_ck, cfg.B, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dev)
+        ck_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        kda.chunk_fwd_ckpt(x["q"], x["k"], x["v"], x["g"], x["beta"], None, ckpt_every=args.ckpt_every, o=o,
+                           hT=hT, ckpt=ck, stream=stream)
+        for i in range(args.steps):
+            ck_ev[i][0].record(stream)
+            kda.chunk_fwd_ckpt(x["q"], x["k"], x["v"], x["g"], x["beta"], None, ckpt_every=args.ckpt_every, o=o,
+                               hT=hT, ckpt=ck, stream=stream)
+            ck_ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ck_ms = [e[0].elapsed_time(e[1]) for e in ck_ev]
+        del ck
     pre_ms = [e[0].elapsed_time(e[1]) for e in pre_ev]
     dec_ms = [e[0].elapsed_time(e[1]) for e in dec_ev] if d is not None else []
     pre_avg = sum(pre_ms) / len(pre_ms)
@@ -236,6 +253,13 @@ def main():
         result["decode"] = {"workload": dcfg.name, "ms": dec_avg, "achieved": dg, "peak": HBM_PEAK_GBPS,
                             "unit": "GB/s", "frac": dg / HBM_PEAK_GBPS, "alg_bytes_per_launch": dbytes,
                             "traffic": load_traffic("decode")}
+    if ck_ms:
+        ck_avg = sum(ck_ms) / len(ck_ms)
+        n_ck = cfg.T // args.ckpt_every
+        ck_bytes = pbytes + n_ck * cfg.B * cfg.H * 4 * cfg.D * cfg.D
+        result["checkpoints"] = {"every_tokens": args.ckpt_every, "count": n_ck, "ms": ck_avg,
+                                 "overhead": ck_avg / pre_avg - 1.0, "alg_bytes_per_launch": ck_bytes,
+                                 "achieved_GBps": ck_bytes / (ck_avg * 1e-3) / 1e9}
     if not args.no_cpu_baseline:
         del x, o, hT
         log("cpu baseline (oracle), ~%.0f s" % args.cpu_seconds)

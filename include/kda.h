@@ -89,6 +89,31 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
                          kda_dtype in_dtype, float scale, void *stream);
 
 /*
+ * kda_chunk_fwd_ckpt -- kda_chunk_fwd that also writes the state every
+ * ckpt_every tokens: the sparse KDA state checkpoints of the Kimi K3 paper
+ * digest (devpress.csdn.net), section 2.4 (4), from which a cached prefix can
+ * be resumed.
+ *
+ *   ckpt        [n_ckpt, B, H, Dk, Dv] fp32, written, n_ckpt = T / ckpt_every
+ *               rounded down.  Checkpoint i is the state after the first
+ *               (i + 1) * ckpt_every tokens, laid out like h0, so any one of
+ *               them can be passed back as h0 to continue from that token.
+ *               It must not overlap any other argument.  NULL = no
+ *               checkpoints (the call is then exactly kda_chunk_fwd).
+ *   ckpt_every  tokens between checkpoints, a positive multiple of the
+ *               16-token chunk; ignored when ckpt is NULL.
+ *
+ * All other arguments, the layouts and the errors are those of kda_chunk_fwd;
+ * a ckpt_every that is not a positive multiple of 16 is
+ * KDA_ERR_INVALID_ARGUMENT.
+ */
+kda_status kda_chunk_fwd_ckpt(const void *q, const void *k, const void *v,
+                              const float *g, const float *beta, const float *h0,
+                              float *o, float *hT, float *ckpt, int64_t ckpt_every,
+                              int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                              kda_dtype in_dtype, float scale, void *stream);
+
+/*
  * kda_decode_step -- one new token per sequence (recurrent decoding, the case
  * behind the 4x decoding speed-up at 1M tokens quoted in "Kimi K3
  * Architecture Explained", section 3): the recurrence above with T = 1,

@@ -52,6 +52,9 @@ def library() -> ctypes.CDLL:
             lib.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, i64, i64, i64, i64, i64,
                                           ctypes.c_int, ctypes.c_float, vp]
             lib.kda_chunk_fwd.restype = ctypes.c_int
+            lib.kda_chunk_fwd_ckpt.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, fp, i64, i64, i64, i64, i64, i64,
+                                               ctypes.c_int, ctypes.c_float, vp]
+            lib.kda_chunk_fwd_ckpt.restype = ctypes.c_int
             lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, i64, i64, i64, i64,
                                             ctypes.c_int, ctypes.c_float, vp]
             lib.kda_decode_step.restype = ctypes.c_int
@@ -138,6 +141,51 @@ def chunk_fwd(q, k, v, g, beta, h0=None, *, scale: float | None = None, o=None, 
     _check(lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
                              B, T, H, Dk, Dv, _dtype_code(q), float(scale or 0.0), _stream(stream)))
     return o, hT
+
+
+def chunk_fwd_ckpt(q, k, v, g, beta, h0=None, *, ckpt_every: int, scale: float | None = None, o=None,
+                   hT=None, ckpt=None, output_final_state: bool = True, stream=None):
+    """Chunked KDA prefill that also returns state checkpoints (``kda_chunk_fwd_ckpt``).
+
+    Arguments as in :func:`chunk_fwd`; ``ckpt_every`` is the number of tokens
+    between checkpoints (a positive multiple of 16).  Returns (o, hT, ckpt)
+    with ckpt [T // ckpt_every, B, H, Dk, Dv] fp32: ckpt[i] is the state
+    after the first (i + 1) * ckpt_every tokens, usable as ``h0``.
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.float32)
+    if hT is None and output_final_state:
+        hT = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if hT is not None:
+        _need(hT, "hT", torch.float32)
+    n_ckpt = T // ckpt_every if ckpt_every > 0 else 0
+    if ckpt is None:
+        ckpt = torch.empty((n_ckpt, B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    _need(ckpt, "ckpt", torch.float32)
+    shapes_ok = (k.shape == q.shape and g.shape == q.shape and v.shape[:3] == (B, T, H)
+                 and beta.shape == (B, T, H) and o.shape == (B, T, H, Dv)
+                 and (h0 is None or h0.shape == (B, H, Dk, Dv))
+                 and (hT is None or hT.shape == (B, H, Dk, Dv))
+                 and ckpt.shape == (n_ckpt, B, H, Dk, Dv))
+    if not shapes_ok:
+        raise ValueError("inconsistent shapes")
+    lib = library()
+    # with no checkpoint to write (T < ckpt_every) the tensor is empty and may have no storage; a
+    # non-null placeholder keeps ckpt_every validated by the library, which never touches ckpt then
+    ck = _ptr(ckpt) if ckpt.numel() > 0 else ctypes.c_void_p(16)
+    _check(lib.kda_chunk_fwd_ckpt(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
+                                  ck, int(ckpt_every), B, T, H, Dk, Dv, _dtype_code(q), float(scale or 0.0),
+                                  _stream(stream)))
+    return o, hT, ckpt
 
 
 def decode_step(q, k, v, g, beta, state, *, scale: float | None = None, o=None, stream=None):

@@ -125,9 +125,14 @@ const char *kda_last_error(void) { return g_last_error; }
 
 int kda_version(void) { return 100; }  // 0.1.0
 
-kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                         const float *h0, float *o, float *hT, int64_t B, int64_t T, int64_t H, int64_t Dk,
-                         int64_t Dv, kda_dtype in_dtype, float scale, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The prefill entry points: kda_chunk_fwd is this with no checkpoints.
+kda_status chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                     const float *h0, float *o, float *hT, float *ckpt, int64_t ckpt_every, int64_t B, int64_t T,
+                     int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale, void *stream) {
     if (B <= 0 || H <= 0 || Dk <= 0 || Dv <= 0 || T < 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "sizes must be positive (T >= 0): B=%lld T=%lld H=%lld Dk=%lld Dv=%lld",
                     (long long)B, (long long)T, (long long)H, (long long)Dk, (long long)Dv);
@@ -139,6 +144,10 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
     if (T > 0 && (!q || !k || !v || !g || !beta || !o))
         return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and o must be non-null when T > 0");
     if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
+    if (ckpt && (ckpt_every <= 0 || ckpt_every % kda::kChunk != 0))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "ckpt_every=%lld must be a positive multiple of %d",
+                    (long long)ckpt_every, kda::kChunk);
+    const int64_t n_ckpt = ckpt ? T / ckpt_every : 0;
 
     uint64_t n_tok = 1, n_state = 1;
     if (!mul_ok(n_tok, B) || !mul_ok(n_tok, T) || !mul_ok(n_tok, H) || !mul_ok(n_state, B) ||
@@ -148,13 +157,17 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
     if (!mul_ok(n_qk, Dk) || !mul_ok(n_v, Dv) || n_qk > UINT64_MAX / 8)
         return fail(KDA_ERR_INVALID_ARGUMENT, "tensor sizes overflow 64 bits");
     if (B * H * 64 > INT32_MAX) return fail(KDA_ERR_UNSUPPORTED, "B*H too large for one launch");
+    uint64_t n_ck = n_state;
+    if (!mul_ok(n_ck, n_ckpt) || n_ck > UINT64_MAX / 4)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "tensor sizes overflow 64 bits");
     const uint64_t esz = in_dtype == KDA_BF16 ? 2 : 4;
 
     const Span sp[] = {
         {"q", q, n_qk * esz}, {"k", k, n_qk * esz},    {"v", v, n_v * esz},         {"g", g, n_qk * 4},
         {"beta", beta, n_tok * 4}, {"h0", h0, n_state * 4}, {"o", o, n_v * 4}, {"hT", hT, n_state * 4},
+        {"ckpt", n_ckpt > 0 ? ckpt : nullptr, n_ck * 4},
     };
-    constexpr int kO = 6, kHT = 7, kH0 = 5;
+    constexpr int kO = 6, kHT = 7, kH0 = 5, kCk = 8;
     for (int i = 0; i < 8; ++i) {
         if (i != kO && overlaps(sp[kO], sp[i]))
             return fail(KDA_ERR_INVALID_ARGUMENT, "o overlaps %s", sp[i].name);
@@ -164,13 +177,19 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
     }
     if (overlaps(sp[kHT], sp[kH0]) && hT != h0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "hT partially overlaps h0 (only an exact alias is allowed)");
+    for (int i = 0; i < 8; ++i) {
+        if (overlaps(sp[kCk], sp[i])) return fail(KDA_ERR_INVALID_ARGUMENT, "ckpt overlaps %s", sp[i].name);
+    }
     kda_status st = check_device();
     if (st != KDA_OK) return st;
-    st = check_spans(sp, 8);
+    st = check_spans(sp, 9);
     if (st != KDA_OK) return st;
 
     kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.hT = hT;
+    a.ckpt = n_ckpt > 0 ? ckpt : nullptr;
+    a.ckpt_every = ckpt ? ckpt_every / kda::kChunk : 0;
+    a.n_ckpt = n_ckpt;
     a.B = B; a.T = T; a.H = H; a.D = static_cast<int>(Dk);
     a.bf16 = in_dtype == KDA_BF16;
     a.scale = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(Dk));
@@ -178,6 +197,23 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (kda::prefill_mfma_supported(a)) return launch_status(kda::launch_prefill_mfma(a, s), "kda prefill (mfma)");
     return launch_status(kda::launch_prefill_valu(a, s), "kda prefill (valu)");
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                         const float *h0, float *o, float *hT, int64_t B, int64_t T, int64_t H, int64_t Dk,
+                         int64_t Dv, kda_dtype in_dtype, float scale, void *stream) {
+    return chunk_fwd(q, k, v, g, beta, h0, o, hT, nullptr, 0, B, T, H, Dk, Dv, in_dtype, scale, stream);
+}
+
+kda_status kda_chunk_fwd_ckpt(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                              const float *h0, float *o, float *hT, float *ckpt, int64_t ckpt_every, int64_t B,
+                              int64_t T, int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale,
+                              void *stream) {
+    return chunk_fwd(q, k, v, g, beta, h0, o, hT, ckpt, ckpt_every, B, T, H, Dk, Dv, in_dtype, scale, stream);
 }
 
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,

@@ -15,6 +15,9 @@ struct PrefillArgs {
     const float *h0;         // [B,H,D,D] or null
     float *o;                // [B,T,H,D]
     float *hT;               // [B,H,D,D] or null (may equal h0)
+    float *ckpt;             // [n_ckpt,B,H,D,D] or null: state after every ckpt_every chunks
+    int64_t ckpt_every;      // chunks between checkpoints (>= 1 when ckpt is set)
+    int64_t n_ckpt;          // checkpoints to write
     int64_t B, T, H;
     int D;
     bool bf16;

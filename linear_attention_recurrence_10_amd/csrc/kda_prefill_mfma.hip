@@ -530,6 +530,9 @@ __device__ __forceinline__ void run_steps(int64_t nchunks, Body &&body) {
     __syncthreads();
 }
 
+// CKPT: the launch writes state checkpoints (a separate instantiation, so that
+// the plain prefill carries no test for them).
+template <bool CKPT>
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     __shared__ Smem sm;
 
@@ -618,12 +621,25 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             if constexpr (decltype(solve_tag)::value) solve(sm, PAR ^ 1, sv, grp, n16, lane);
         });
     } else {
-        int sslot = 1;  // ring slot of chunk n (n = -2 maps to slot 1)
+        int sslot = 1;        // ring slot of chunk n (n = -2 maps to slot 1)
+        int64_t ck_left = a.ckpt_every, ck_i = 0;  // chunks to the next checkpoint, its index
         run_steps(nchunks, [&](auto par_tag, auto, auto, auto state_tag, int64_t n) {
             constexpr int PAR = decltype(par_tag)::value;
             if constexpr (decltype(state_tag)::value) {
                 state_chunk(a, sm, sm.ops[sslot], PAR, n, n * kC, vraw[PAR], S, b, h, rh, ct, grp, n16, lane, col);
                 load_v(vraw[PAR], a, min((n + 2) * kC, last_t0), b, h, col, grp, voff);
+                if (CKPT && --ck_left == 0) {  // the state after (ck_i + 1) * ckpt_every chunks
+                    if (ck_i < a.n_ckpt) {
+                        float *ck = a.ckpt + ck_i * (BH * kD * kD) + sbase;
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) ck[(64 * rh + 16 * t + 4 * grp + i) * kD + col] = S[t][i];
+                        }
+                    }
+                    ++ck_i;
+                    ck_left = a.ckpt_every;
+                }
             }
             sslot = (sslot == kRing - 1) ? 0 : sslot + 1;
         });
@@ -654,7 +670,10 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
     const int64_t BH = a.B * a.H;
     const int64_t rounds = (BH + 7) / 8;
     dim3 grid(static_cast<unsigned>(rounds * 8 * kNV)), block(kThreads);
-    hipLaunchKernelGGL(prefill_mfma_kernel, grid, block, 0, s, a);
+    if (a.ckpt)
+        hipLaunchKernelGGL(prefill_mfma_kernel<true>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(prefill_mfma_kernel<false>, grid, block, 0, s, a);
     return hipGetLastError();
 }
 

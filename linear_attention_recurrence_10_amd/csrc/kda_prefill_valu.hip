@@ -68,6 +68,7 @@ __global__ __launch_bounds__(DVS *RG) void prefill_valu_kernel(PrefillArgs a) {
     }
 
     const int64_t nchunks = (T + C - 1) / C;
+    int64_t ck_left = a.ckpt_every, ck_i = 0;  // chunks to the next checkpoint, its index
     for (int64_t n = 0; n < nchunks; ++n) {
         const int64_t t0 = n * C;
         // (1) stage q, k, g (C x D), the value slice and beta; tokens past T are
@@ -201,6 +202,15 @@ __global__ __launch_bounds__(DVS *RG) void prefill_valu_kernel(PrefillArgs a) {
 #pragma unroll
             for (int r = 0; r < C; ++r) acc += sKd[r][i] * u[r];
             S[m] = acc;
+        }
+        if (a.ckpt && --ck_left == 0) {  // the state after (ck_i + 1) * ckpt_every chunks
+            if (ck_i < a.n_ckpt) {
+                float *ck = a.ckpt + ck_i * (a.B * H * static_cast<int64_t>(D) * D) + sbase;
+#pragma unroll
+                for (int m = 0; m < RPT; ++m) ck[static_cast<int64_t>(rg + RG * m) * D + col] = S[m];
+            }
+            ++ck_i;
+            ck_left = a.ckpt_every;
         }
         __syncthreads();  // LDS is reused by the next chunk
     }

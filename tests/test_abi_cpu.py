@@ -30,7 +30,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("kda_chunk_fwd", "kda_decode_step", "kda_status_string", "kda_last_error", "kda_version"):
+    for n in ("kda_chunk_fwd", "kda_chunk_fwd_ckpt", "kda_decode_step", "kda_status_string", "kda_last_error",
+              "kda_version"):
         assert n in names
 
 
@@ -124,3 +125,29 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 16, 1, 16)
     with pytest.raises(ValueError):
         kda.chunk_fwd(x, x, x, x.float(), torch.zeros(1, 16, 1))
+
+
+def chunk_ckpt(lib, every=64, T=256, ptrs=None):
+    p = ptrs or [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(9)]
+    return lib.kda_chunk_fwd_ckpt(*p[:9], every, 1, T, 1, 128, 128, 1, 0.0, None)
+
+
+@pytest.mark.parametrize("every", [0, -16, 8, 40])
+def test_ckpt_interval_must_be_a_chunk_multiple(lib, every):
+    assert chunk_ckpt(lib, every=every) == 1
+    assert b"multiple of 16" in lib.kda_last_error()
+
+
+def test_ckpt_must_not_overlap(lib):
+    ptrs = [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(9)]
+    ptrs[8] = ctypes.c_void_p(ptrs[6].value + 4096)   # inside o
+    assert chunk_ckpt(lib, ptrs=ptrs) == 1
+    assert b"ckpt overlaps o" in lib.kda_last_error()
+
+
+def test_ckpt_null_ignores_interval(lib):
+    ptrs = [P] * 9
+    ptrs[8] = None
+    ptrs[0] = None    # then the first error is the null input, not the interval
+    assert chunk_ckpt(lib, every=7, ptrs=ptrs) == 1
+    assert b"non-null" in lib.kda_last_error()

@@ -1,0 +1,95 @@
+"""State checkpoints (kda_chunk_fwd_ckpt) against the fp64 oracle.
+
+Checkpoint i must equal the state after the first (i + 1) * ckpt_every tokens:
+the oracle computes that state by running the token recurrence on exactly
+that prefix.  Checkpointing must leave o and hT bit-identical to
+kda_chunk_fwd, and a checkpoint passed back as h0 must resume the sequence.
+"""
+from __future__ import annotations
+
+import sys
+
+import pytest
+import torch
+
+import kda_inputs
+import linear_attention_recurrence_10_amd as kda
+from gpu_helpers import oracle_full, rel_err, tol_for
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def fwd_ckpt(x, every, h0=None):
+    return kda.chunk_fwd_ckpt(x["q"], x["k"], x["v"], x["g"], x["beta"], h0, ckpt_every=every)
+
+
+def prefix(x, t1):
+    return {n: x[n][:, :t1].contiguous() for n in ("q", "k", "v", "g", "beta")}
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 128), ("f32", 16)])
+@pytest.mark.parametrize("T,every", [(200, 48), (256, 64), (37, 16), (96, 16)])
+def test_checkpoints_match_oracle_prefix_states(dtype, D, T, every):
+    say("case ckpt dtype=%s D=%d T=%d every=%d" % (dtype, D, T, every))
+    x = kda_inputs.prefill_inputs(2, T, 3, D, dtype, h0=True, seed=61, device=DEV)
+    o, hT, ck = fwd_ckpt(x, every, x["h0"])
+    torch.cuda.synchronize()
+    assert ck.shape == (T // every, 2, 3, D, D)
+    tol = tol_for(dtype)
+    for i in range(T // every):
+        _, s_ref = oracle_full(prefix(x, (i + 1) * every), h0=x["h0"])
+        e = rel_err(ck[i].cpu(), s_ref)
+        say("  ckpt %d (%d tokens): err=%.3e" % (i, (i + 1) * every, e))
+        assert e <= tol, (i, e)
+    o_ref, h_ref = oracle_full(x)
+    assert rel_err(o.cpu(), o_ref) <= tol and rel_err(hT.cpu(), h_ref) <= tol
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 16)])
+def test_checkpointing_leaves_outputs_unchanged(dtype, D):
+    x = kda_inputs.prefill_inputs(1, 320, 4, D, dtype, h0=True, seed=62, device=DEV)
+    o1, h1 = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+    o2, h2, ck = fwd_ckpt(x, 64, x["h0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    assert torch.equal(ck[-1], h2)   # T is a multiple of ckpt_every: the last checkpoint is the final state
+
+
+def test_resume_from_checkpoint():
+    """A checkpoint used as h0 continues the sequence (prefix reuse)."""
+    x = kda_inputs.prefill_inputs(2, 512, 4, 128, "bf16", h0=True, seed=63, device=DEV)
+    o, hT, ck = fwd_ckpt(x, 128, x["h0"])
+    rest = {n: x[n][:, 256:].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    o2, h2 = kda.chunk_fwd(rest["q"], rest["k"], rest["v"], rest["g"], rest["beta"], ck[1].contiguous())
+    torch.cuda.synchronize()
+    assert rel_err(o2.cpu(), o[:, 256:].cpu()) < 1e-3 and rel_err(h2.cpu(), hT.cpu()) < 1e-3
+
+
+def test_sequence_shorter_than_interval():
+    x = kda_inputs.prefill_inputs(1, 40, 2, 128, "bf16", h0=True, seed=64, device=DEV)
+    o1, h1 = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+    o2, h2, ck = fwd_ckpt(x, 48, x["h0"])
+    torch.cuda.synchronize()
+    assert ck.shape[0] == 0 and torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def test_checkpoints_full_width_sampled():
+    """56 heads x 4096 tokens, checkpoints every 512 tokens: two heads checked against the oracle."""
+    x = kda_inputs.prefill_inputs(1, 4096, 56, 128, "bf16", seed=65, device=DEV)
+    _, _, ck = fwd_ckpt(x, 512)
+    torch.cuda.synchronize()
+    heads = [0, 37]
+    hi = torch.as_tensor(heads, device=DEV)
+    for i in (0, 3, 7):
+        t1 = (i + 1) * 512
+        sub = {n: x[n][:, :t1].index_select(2, hi).contiguous() for n in ("q", "k", "v", "g", "beta")}
+        _, s_ref = oracle_full(sub)
+        e = rel_err(ck[i].index_select(1, hi).cpu(), s_ref)
+        say("  ckpt %d: err=%.3e" % (i, e))
+        assert e <= tol_for("bf16")
