@@ -38,10 +38,14 @@
 //    ct) holds state rows [64 rh, 64 rh + 64) x columns 16 ct .. 16 ct + 15
 //    in registers and runs the state part of chunk n.  The two row halves of
 //    a column tile exchange their partial X, Y through LDS with a flag
-//    handshake; both then form the same U for their own rows.
+//    handshake; both then form the same U for their own rows.  They read a
+//    chunk's operands into registers during the step before its own, so
+//    the state step waits on LDS only for M, P and the partner's partials.
 // One work-group barrier per chunk hands the k-side of later chunks to the
-// state waves; one wave of each role shares each SIMD, so one's vector work
-// fills the others' matrix-core, LDS and dependency latency.
+// state waves; one wave of each role shares each SIMD.  The state waves run
+// at a raised wave priority: their chain from chunk to chunk sets the pace,
+// and the other two roles (which work ahead) fill the SIMD's spare issue
+// cycles.
 //
 // Operand layouts (lane l, row group g = l / 16, n = l % 16):
 //   16x16x16 (bf16_1k):  A[m = n][k = 4g + i],  B[k = 4g + i][col = n]
@@ -59,6 +63,7 @@
 // with the identity converts it exactly (its inputs are bf16).  The
 // Grams are formed transposed (Kh Kb^T, Kh Qb^T), so their result layout is
 // "row n, columns 4g + i", the A-operand layout of U = M Z and P U.
+#include <cstdlib>
 #include <type_traits>
 
 #include "kda_internal.h"
@@ -173,10 +178,12 @@ __device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p 
 __device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
 __device__ __forceinline__ float bf16_bits(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
-// DPP data movement inside each 16-lane row.
+// DPP data movement inside each 16-lane row.  A lane whose source lies
+// outside its row (row shifts) reads 0 (bound_ctrl), which is what the prefix
+// sums need and lets the move fold into the instruction that uses it.
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
 }
 template <int U>
 __device__ __forceinline__ float row_bcast(float x) {  // lane U of the row to the whole row
@@ -196,21 +203,21 @@ __device__ __forceinline__ void tri_pivots(float &x, const float (&ar)[kC]) {
     }
 }
 
-// One chunk's k-side operands in the lane order the state waves read them
-// (every access is lane-contiguous).
+// Everything the state waves need of one chunk, in the lane order they read
+// it (every access is lane-contiguous): one slot of the LDS ring.
 struct Ops {
     bf16x8 qk[2][4][2][64];  // [Qb, Kb][32-channel quarter][hi, lo][lane], token per lane
     bf16x4 kht[8][2][64];    // [16-channel tile][hi, lo][lane], Kh channel per lane
-    f32x4 eC[kD / 4];        // e^gamma_C of channels 4i .. 4i + 3
+    f32x4 eq[2][4][4];       // e^gamma_C: [rh][g][q] holds channels 64 rh + 16 t + 4 g + q, t = 0..3
+    bf16x4 Mhl[2][64];       // M = (I + A)^-1 diag(beta), split [hi, lo][lane], A-operand layout
+    f32x4 P[64];             // P: lane (n, g) holds row n, columns 4g .. 4g + 3
 };
 
 struct Smem {
-    Ops ops[kRing];
+    Ops ops[kRing];               // chunks n, n + 1, n + 2
     f32x4 gram[2][4][2][64];      // partial Grams [parity][k-side wave][A, P][lane]
-    f32x4 arow[4][kC][5];         // summed, masked A per solver wave; rows padded to 80 bytes
-    bf16x4 Mhl[2][2][64];         // M = (I + A)^-1 diag(beta), split [parity][hi, lo][lane], A-operand layout
-    alignas(16) float P[2][kC][20];  // P [parity][row][column], padded rows
     float beta[2][kC];
+    f32x4 arow[4][kC][5];         // summed, masked A per solver wave; rows padded to 80 bytes
     f32x4 xy[2][2][2][64];        // partial X, Y [row half][X, Y][column tile][lane]
     uint32_t flag[2][2];          // state-wave handshake [column tile][row half]
 };
@@ -311,10 +318,10 @@ __device__ __forceinline__ void kside_in(const PrefillArgs &a, const KRaw &raw, 
     }
 }
 
-// K-side, second part: this quarter's operands of the chunk go to `op`, its
-// partial Grams and beta to the `par` buffers.
-__device__ __forceinline__ void kside(Smem &sm, Ops &op, const KIn &in, int par, int kw, int grp, int n16, int lane,
-                                      const bf16x4 &ident) {
+// K-side, second part: this quarter's operands of the chunk go to `op` (LDS or
+// a shared slot in global memory), its partial Grams to `gr`, beta to `bt`.
+__device__ __forceinline__ void kside(Ops &op, f32x4 (&gr)[4][2][64], float (&bt)[kC], const KIn &in, int kw,
+                                      int grp, int n16, int lane, const bf16x4 &ident) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const float(&gv)[8] = in.g;
     const float(&qv)[8] = in.q;
@@ -358,41 +365,44 @@ __device__ __forceinline__ void kside(Smem &sm, Ops &op, const KIn &in, int par,
     op.kht[2 * kw + 1][0][lane] = transpose_tile(last4(Kh.hi), ident);
     op.kht[2 * kw + 1][1][lane] = transpose_tile(last4(Kh.lo), ident);
     if (n16 == 0) {
-        op.eC[8 * kw + grp] = f32x4{eC[0], eC[1], eC[2], eC[3]};
-        op.eC[8 * kw + 4 + grp] = f32x4{eC[4], eC[5], eC[6], eC[7]};
+        // slots j < 4 of row g are channels 32 kw + 4 g + j, i.e. row half kw / 2, tile
+        // t = 2 (kw % 2), q = j; slots j >= 4 the same q in tile t + 1
+#pragma unroll
+        for (int q = 0; q < 4; ++q) reinterpret_cast<f32x2 *>(&op.eq[kw >> 1][grp][q])[kw & 1] = f32x2{eC[q], eC[q + 4]};
     }
-    if (kw == 0 && grp == 0) sm.beta[par][n16] = in.beta;
+    if (kw == 0 && grp == 0) bt[n16] = in.beta;
     // partial Grams over this quarter, transposed:
     // mm32(Kh, Kb)[m][n] = Kh_m . Kb_n = (Kb Kh^T)[n][m], so lane (n, g) gets row n, columns 4g + i
-    sm.gram[par][kw][0][lane] = mm32(Kh, Kb, zero);
-    sm.gram[par][kw][1][lane] = mm32(Kh, Qb, zero);
+    gr[kw][0][lane] = mm32(Kh, Kb, zero);
+    gr[kw][1][lane] = mm32(Kh, Qb, zero);
 }
 
 // M = (I + A)^-1 diag(beta) and P of the chunk whose Grams sit in the `par`
 // buffers: solver wave kw solves columns 4 kw .. 4 kw + 3, one per 16-lane row.
-__device__ __forceinline__ void solve(Smem &sm, int par, int kw, int grp, int n16, int lane) {
+__device__ __forceinline__ void solve(const f32x4 (&gr)[4][2][64], const float (&bt)[kC], f32x4 (&arow)[kC][5],
+                                      bf16x4 (&Mo)[2][64], f32x4 (&Po)[64], int kw, int grp, int n16, int lane) {
     // lane (row r = n, column group g): sum the partial Grams of row r, columns 4g .. 4g + 3
-    f32x4 as = sm.gram[par][0][0][lane], ps = sm.gram[par][0][1][lane];
+    f32x4 as = gr[0][0][lane], ps = gr[0][1][lane];
 #pragma unroll
     for (int ww = 1; ww < 4; ++ww) {
-        as += sm.gram[par][ww][0][lane];
-        ps += sm.gram[par][ww][1][lane];
+        as += gr[ww][0][lane];
+        ps += gr[ww][1][lane];
     }
-    const float beta_r = sm.beta[par][n16];
+    const float beta_r = bt[n16];
     f32x4 av;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         av[i] = (4 * grp + i < n16) ? beta_r * as[i] : 0.f;
         ps[i] = (4 * grp + i <= n16) ? ps[i] : 0.f;
     }
-    sm.arow[kw][n16][grp] = av;
+    arow[n16][grp] = av;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     float ar[kC];  // row n of A
 #pragma unroll
     for (int u4 = 0; u4 < 4; ++u4) {
-        const f32x4 row = sm.arow[kw][n16][u4];
+        const f32x4 row = arow[n16][u4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) ar[4 * u4 + j] = row[j];
     }
@@ -401,37 +411,55 @@ __device__ __forceinline__ void solve(Smem &sm, int par, int kw, int grp, int n1
     tri_pivots<0>(x, ar);
     // M[n][s] goes to slot s % 4 = grp of lane 16 (s / 4) + n = 16 kw + n of
     // the A operand of U = M Z, as a hi/lo bf16 pair
-    const float m = x * sm.beta[par][s];
+    const float m = x * bt[s];
     const __bf16 mh = static_cast<__bf16>(m);
     const __bf16 ml = static_cast<__bf16>(m - static_cast<float>(mh));
-    reinterpret_cast<__bf16 *>(&sm.Mhl[par][0][16 * kw + n16])[grp] = mh;
-    reinterpret_cast<__bf16 *>(&sm.Mhl[par][1][16 * kw + n16])[grp] = ml;
+    reinterpret_cast<__bf16 *>(&Mo[0][16 * kw + n16])[grp] = mh;
+    reinterpret_cast<__bf16 *>(&Mo[1][16 * kw + n16])[grp] = ml;
     // every solver wave forms the same P (same sums in the same order) and
     // stores it (no branch on the wave index)
-    *reinterpret_cast<f32x4 *>(&sm.P[par][n16][4 * grp]) = ps;
+    Po[lane] = ps;
+}
+
+// Operands of one chunk that a state wave holds in registers.  They are read
+// during the step before their own (the k-side finished them one step before
+// that): Kb and Qb once that step's X and Y are formed, Kh^T and e^gamma_C
+// once its update has consumed its own.  The reads then have a whole step
+// to land, and the state step itself waits only for M and P.
+struct SOps {
+    Sp8 Kb[2], Qb[2];  // channels of quarters 2 rh + js, operand layout
+    Sp4 KhT[4];        // 16-channel tiles 4 rh + t, channel per lane
+    f32x4 eq;          // e^gamma_C of channels 64 rh + 16 t + 4 g + (n & 3), t = 0..3
+};
+__device__ __forceinline__ void read_kq(SOps &s, const Ops &op, int rh, int lane) {
+#pragma unroll
+    for (int js = 0; js < 2; ++js) {
+        s.Kb[js] = Sp8{op.qk[1][2 * rh + js][0][lane], op.qk[1][2 * rh + js][1][lane]};
+        s.Qb[js] = Sp8{op.qk[0][2 * rh + js][0][lane], op.qk[0][2 * rh + js][1][lane]};
+    }
+}
+__device__ __forceinline__ void read_kh(SOps &s, const Ops &op, int rh, int grp, int n16, int lane) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) s.KhT[t] = Sp4{op.kht[4 * rh + t][0][lane], op.kht[4 * rh + t][1][lane]};
+    s.eq = op.eq[rh][grp][n16 & 3];
+}
+// lane I of each group of four lanes, to the whole group (DPP quad_perm [I, I, I, I])
+template <int I>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return dpp_move<I * 0x55>(x);
 }
 
 // State part of chunk n (start t0) for state wave (rh, ct): X, Y, U, O and
 // the state update S = diag(e^gamma_C) (S0 + Kh^T U) of this wave's rows.
-__device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, const Ops &op, int par, int64_t n,
-                                            int64_t t0, const uint16_t (&vr)[4], f32x4 (&S)[4], int64_t b,
-                                            int64_t h, int rh, int ct, int grp, int n16, int lane, int col) {
+// `op` is chunk n's ring slot (M, P are read from it here; the rest is in
+// `cur`), `nx` chunk n + 1's, whose operands are read into `nxt`.
+__device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, const Ops &op, const Ops &nx, int64_t n,
+                                            int64_t t0, const uint16_t (&vr)[4], f32x4 (&S)[4], const SOps &cur,
+                                            SOps &nxt, int64_t b, int64_t h, int rh, int ct, int grp, int n16,
+                                            int lane, const uint32_t (&voff)[4]) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    // operands that do not depend on the state, read first
-    Sp8 Kb[2], Qb[2];
-#pragma unroll
-    for (int js = 0; js < 2; ++js) {
-        Kb[js] = Sp8{op.qk[1][2 * rh + js][0][lane], op.qk[1][2 * rh + js][1][lane]};
-        Qb[js] = Sp8{op.qk[0][2 * rh + js][0][lane], op.qk[0][2 * rh + js][1][lane]};
-    }
-    Sp4 KhT[4];
-    f32x4 eC[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        KhT[t] = Sp4{op.kht[4 * rh + t][0][lane], op.kht[4 * rh + t][1][lane]};
-        eC[t] = op.eC[16 * rh + 4 * t + grp];
-    }
-    const Sp4 Mf = Sp4{sm.Mhl[par][0][lane], sm.Mhl[par][1][lane]};
+    const Sp4 Mf = Sp4{op.Mhl[0][lane], op.Mhl[1][lane]};
+    const f32x4 Prow = op.P[lane];
 
     // partial X = Kb S0 and Y = Qb S0 over this wave's 64 channels; the state
     // rows of tiles 2js, 2js + 1 are the channels of operand slots 0..3, 4..7
@@ -441,11 +469,14 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
         const float sv[8] = {S[2 * js][0],     S[2 * js][1],     S[2 * js][2],     S[2 * js][3],
                              S[2 * js + 1][0], S[2 * js + 1][1], S[2 * js + 1][2], S[2 * js + 1][3]};
         const Sp8 Sb = split8(sv);
-        X = mm32(Kb[js], Sb, X);
-        Y = mm32(Qb[js], Sb, Y);
+        X = mm32(cur.Kb[js], Sb, X);
+        Y = mm32(cur.Qb[js], Sb, Y);
     }
     sm.xy[rh][0][ct][lane] = X;
     if (rh == 1) sm.xy[1][1][ct][lane] = Y;
+    // Y is formed here in both halves (so that Qb dies before the next
+    // chunk's operands land in other registers)
+    asm volatile("" ::"v"(Y));
     // hand the partials to the other row half of this column tile and wait
     // for its own: its flag reaches n + 1 in this chunk and cannot move
     // further before the next work-group barrier
@@ -455,7 +486,13 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
     while (__hip_atomic_load(&sm.flag[ct][rh ^ 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != tag)
         __builtin_amdgcn_s_sleep(1);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    X += sm.xy[rh ^ 1][0][ct][lane];
+    const f32x4 Xo = sm.xy[rh ^ 1][0][ct][lane];
+    const f32x4 Yo = sm.xy[1][1][ct][lane];  // row half 1's Y (used by row half 0)
+    // the next chunk's Kb, Qb replace this chunk's (dead after X, Y); issued
+    // after the handshake so that no flag poll waits for them
+    asm volatile("" ::: "memory");
+    read_kq(nxt, nx, rh, lane);
+    X += Xo;
 
     f32x4 vv;
 #pragma unroll
@@ -463,23 +500,34 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
     const Sp4 U = split4(mm16(Mf, split4(vv - X), zero));
 
     if (rh == 0) {
-        Y += sm.xy[1][1][ct][lane];
-        const f32x4 Prow = *reinterpret_cast<const f32x4 *>(&sm.P[par][n16][4 * grp]);
-        const f32x4 O = mm16(split4(Prow), U, Y);
-        const int64_t T = a.T, H = a.H;
-        char *ob = reinterpret_cast<char *>(a.o + ((b * T + t0) * H + h) * kD);  // wave uniform
-        const int HD = static_cast<int>(H) * kD;
+        const f32x4 O = mm16(split4(Prow), U, Y + Yo);
+        // o has the layout of v: token 4g + i, column `col` at element offset voff[i]
+        char *ob = reinterpret_cast<char *>(a.o + ((b * a.T + t0) * a.H + h) * kD);  // wave uniform
+        if (t0 + kC <= a.T) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (t0 + 4 * grp + i < T)
-                *reinterpret_cast<float *>(ob + 4u * static_cast<uint32_t>((4 * grp + i) * HD + col)) =
-                    a.scale * O[i];
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<float *>(ob + 4u * voff[i]) = a.scale * O[i];
+        } else {
+            const int left = static_cast<int>(a.T - t0);  // tokens of the last, partial chunk
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (4 * grp + i < left) *reinterpret_cast<float *>(ob + 4u * voff[i]) = a.scale * O[i];
+            }
         }
     }
 
-    // S: lane (n, g) holds rows 4g + i of each tile, the channels of eC[t]
+    // S: lane (n, g) holds rows 4g + i of tile t, channel 64 rh + 16 t + 4 g + i,
+    // whose e^gamma_C sits in component t of lane (4 (n / 4) + i, g)'s eq
 #pragma unroll
-    for (int t = 0; t < 4; ++t) S[t] = eC[t] * mm16(KhT[t], U, S[t]);
+    for (int t = 0; t < 4; ++t) {
+        const f32x4 acc = mm16(cur.KhT[t], U, S[t]);
+        S[t][0] = quad_bcast<0>(cur.eq[t]) * acc[0];
+        S[t][1] = quad_bcast<1>(cur.eq[t]) * acc[1];
+        S[t][2] = quad_bcast<2>(cur.eq[t]) * acc[2];
+        S[t][3] = quad_bcast<3>(cur.eq[t]) * acc[3];
+    }
+    // the update is issued before the next chunk's Kh^T, e^gamma_C are read
+    asm volatile("" ::"v"(S[0]), "v"(S[1]), "v"(S[2]), "v"(S[3]) : "memory");
+    read_kh(nxt, nx, rh, grp, n16, lane);
 }
 
 // The step sequence of a work-group over nchunks chunks, with one barrier
@@ -488,7 +536,24 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
 // n + 2 prepared and chunk n advanced: steps -2 and -1 fill the pipeline,
 // the last two drain it, and every step in between does all three.  Both
 // roles call this with the same nchunks, so they meet the same barriers.
-template <class Body>
+// The barrier that ends a step.  A role whose LDS writes others read in the
+// next step (k-side, solver) waits for its LDS operations first
+// (__syncthreads).  The state waves publish nothing through the barrier
+// (their X, Y exchange has its own flags), and their loads in flight are read
+// ahead of the slot's reuse: they arrive at the barrier without waiting.  The
+// empty asm statements keep the compiler from moving LDS accesses across it.
+template <bool FENCE>
+__device__ __forceinline__ void step_barrier() {
+    if constexpr (FENCE) {
+        __syncthreads();
+    } else {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    }
+}
+
+template <bool FENCE = true, class Body>
 __device__ __forceinline__ void run_steps(int64_t nchunks, Body &&body) {
     using F = std::false_type;
     using Tr = std::true_type;
@@ -500,38 +565,39 @@ __device__ __forceinline__ void run_steps(int64_t nchunks, Body &&body) {
     // are never read): the same load pattern on every path keeps the
     // compiler's load-count bookkeeping exact at the loop entry
     body(P0{}, F{}, Tr{}, F{}, -2);  // k-side of chunk 0
-    __syncthreads();
+    step_barrier<FENCE>();
     body(P1{}, Tr{}, Tr{}, F{}, -1);  // solve of chunk 0, k-side of chunk 1
-    __syncthreads();
+    step_barrier<FENCE>();
+    // steps 0 .. nchunks - 3 do all three; the loop ends on an odd step, so
+    // every step after it has a parity known here (no register buffer has
+    // to survive a step whose parity is decided at run time)
     int64_t n = 0;
     for (; n + 1 < nchunks - 2; n += 2) {  // chunks n + 2 and n + 3 exist
         body(P0{}, Tr{}, Tr{}, Tr{}, n);
-        __syncthreads();
+        step_barrier<FENCE>();
         body(P1{}, Tr{}, Tr{}, Tr{}, n + 1);
-        __syncthreads();
+        step_barrier<FENCE>();
     }
-    if (n < nchunks - 2) {
-        body(P0{}, Tr{}, Tr{}, Tr{}, n);
-        __syncthreads();
-        ++n;
-    }
-    if (n == nchunks - 2) {  // solve of the last chunk
-        if (n & 1)
-            body(P1{}, Tr{}, F{}, Tr{}, n);
-        else
-            body(P0{}, Tr{}, F{}, Tr{}, n);
-        __syncthreads();
-        ++n;
-    }
-    if (n & 1)
-        body(P1{}, F{}, F{}, Tr{}, n);
-    else
+    if (nchunks & 1) {  // n = nchunks - 3 (or nchunks = 1: n = 0 is the last step)
+        if (nchunks > 1) {
+            body(P0{}, Tr{}, Tr{}, Tr{}, n);
+            step_barrier<FENCE>();
+            body(P1{}, Tr{}, F{}, Tr{}, n + 1);  // solve of the last chunk
+            step_barrier<FENCE>();
+            n += 2;
+        }
         body(P0{}, F{}, F{}, Tr{}, n);
-    __syncthreads();
+        step_barrier<FENCE>();
+    } else {  // n = nchunks - 2
+        body(P0{}, Tr{}, F{}, Tr{}, n);  // solve of the last chunk
+        step_barrier<FENCE>();
+        body(P1{}, F{}, F{}, Tr{}, n + 1);
+        step_barrier<FENCE>();
+    }
 }
 
-// CKPT: the launch writes state checkpoints (a separate instantiation, so that
-// the plain prefill carries no test for them).
+// CKPT: the launch writes state checkpoints (a separate instantiation, so the
+// plain prefill carries no test for it).
 template <bool CKPT>
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     __shared__ Smem sm;
@@ -596,11 +662,11 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
         }
     }
 
-    // Step n: the k-side waves solve chunk n + 1 and prepare chunk n + 2
-    // while the state waves run chunk n; one barrier ends the step.  Each
-    // role runs its own copy of the step sequence (see run_steps), so the
-    // register double-buffers of one role never meet the other's in a loop
-    // phi, and loaded values are consumed in the registers they land in.
+    // Step n: the k-side waves prepare chunk n + 2, the solver waves solve
+    // chunk n + 1, the state waves run chunk n; one barrier ends the step.
+    // Each role runs its own copy of the step sequence, so the register
+    // double-buffers of one role never meet another's in a loop phi, and
+    // loaded values are consumed in the registers they land in.
     const int64_t last_t0 = nchunks > 0 ? (nchunks - 1) * kC : 0;
     if (kwave) {
         int kslot = 0;  // ring slot of chunk n + 2
@@ -610,23 +676,34 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             KIn in;
             if constexpr (decltype(kside_tag)::value) kside_in(a, raw[PAR], in, (n + 2) * kC, n16);
             if constexpr (decltype(kside_tag)::value) {
-                kside(sm, sm.ops[kslot], in, PAR, kw, grp, n16, lane, ident);
+                kside(sm.ops[kslot], sm.gram[PAR], sm.beta[PAR], in, kw, grp, n16, lane, ident);
                 load_kraw(raw[PAR], a, min((n + 4) * kC, last_t0), b, h, kw, grp, n16, koff);
             }
             kslot = (kslot == kRing - 1) ? 0 : kslot + 1;
         });
     } else if (!swave) {
+        int vslot = 2;  // ring slot of chunk n + 1 (n = -2 maps to slot 2)
         run_steps(nchunks, [&](auto par_tag, auto solve_tag, auto, auto, int64_t) {
             constexpr int PAR = decltype(par_tag)::value;  // n & 1
-            if constexpr (decltype(solve_tag)::value) solve(sm, PAR ^ 1, sv, grp, n16, lane);
+            if constexpr (decltype(solve_tag)::value)
+                solve(sm.gram[PAR ^ 1], sm.beta[PAR ^ 1], sm.arow[sv], sm.ops[vslot].Mhl, sm.ops[vslot].P, sv, grp,
+                      n16, lane);
+            vslot = (vslot == kRing - 1) ? 0 : vslot + 1;
         });
     } else {
+        // the state waves carry the serial chain from chunk to chunk: the
+        // SIMD issues their instructions first, and the k-side and solver
+        // waves (which work ahead) fill the remaining issue cycles
+        __builtin_amdgcn_s_setprio(3);
         int sslot = 1;        // ring slot of chunk n (n = -2 maps to slot 1)
+        SOps so[2];           // operands of the chunks of even and odd steps
         int64_t ck_left = a.ckpt_every, ck_i = 0;  // chunks to the next checkpoint, its index
-        run_steps(nchunks, [&](auto par_tag, auto, auto, auto state_tag, int64_t n) {
+        run_steps<false>(nchunks, [&](auto par_tag, auto, auto, auto state_tag, int64_t n) {
             constexpr int PAR = decltype(par_tag)::value;
+            const int nslot = (sslot == kRing - 1) ? 0 : sslot + 1;  // chunk n + 1
             if constexpr (decltype(state_tag)::value) {
-                state_chunk(a, sm, sm.ops[sslot], PAR, n, n * kC, vraw[PAR], S, b, h, rh, ct, grp, n16, lane, col);
+                state_chunk(a, sm, sm.ops[sslot], sm.ops[nslot], n, n * kC, vraw[PAR], S, so[PAR], so[PAR ^ 1], b, h,
+                            rh, ct, grp, n16, lane, voff);
                 load_v(vraw[PAR], a, min((n + 2) * kC, last_t0), b, h, col, grp, voff);
                 if (CKPT && --ck_left == 0) {  // the state after (ck_i + 1) * ckpt_every chunks
                     if (ck_i < a.n_ckpt) {
@@ -640,8 +717,12 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
                     ++ck_i;
                     ck_left = a.ckpt_every;
                 }
+            } else if constexpr (PAR == 1) {
+                // step -1: chunk 0 was prepared in step -2; read its operands for step 0
+                read_kq(so[0], sm.ops[nslot], rh, lane);
+                read_kh(so[0], sm.ops[nslot], rh, grp, n16, lane);
             }
-            sslot = (sslot == kRing - 1) ? 0 : sslot + 1;
+            sslot = nslot;
         });
     }
 
@@ -669,11 +750,11 @@ bool prefill_mfma_supported(const PrefillArgs &a) {
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
     const int64_t BH = a.B * a.H;
     const int64_t rounds = (BH + 7) / 8;
-    dim3 grid(static_cast<unsigned>(rounds * 8 * kNV)), block(kThreads);
+    const dim3 grid(static_cast<unsigned>(rounds * 8 * kNV));
     if (a.ckpt)
-        hipLaunchKernelGGL(prefill_mfma_kernel<true>, grid, block, 0, s, a);
+        hipLaunchKernelGGL(prefill_mfma_kernel<true>, grid, dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(prefill_mfma_kernel<false>, grid, block, 0, s, a);
+        hipLaunchKernelGGL(prefill_mfma_kernel<false>, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
