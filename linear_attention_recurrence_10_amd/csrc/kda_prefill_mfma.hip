@@ -195,11 +195,13 @@ __device__ __forceinline__ float row_bcast(float x) {  // lane U of the row to t
 // lives in lane u of the same 16-lane row, so a DPP broadcast replaces any LDS
 // traffic.  A is strictly lower triangular, so rows r <= u are unaffected
 // (A[r][u] = 0).
+// `nar` holds row n of -A, so each pivot is one multiply-add whose DPP
+// broadcast folds into the instruction.
 template <int U>
-__device__ __forceinline__ void tri_pivots(float &x, const float (&ar)[kC]) {
+__device__ __forceinline__ void tri_pivots(float &x, const float (&nar)[kC]) {
     if constexpr (U < kC - 1) {
-        x = __builtin_fmaf(-ar[U], row_bcast<U>(x), x);
-        tri_pivots<U + 1>(x, ar);
+        x = __builtin_fmaf(row_bcast<U>(x), nar[U], x);
+        tri_pivots<U + 1>(x, nar);
     }
 }
 
@@ -331,7 +333,10 @@ __device__ __forceinline__ void kside(Ops &op, f32x4 (&gr)[4][2][64], float (&bt
     // written several instructions earlier (no hazard stalls)
     float gam[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) gam[j] = gv[j] * kLog2e;
+    for (int j = 0; j < 8; ++j) {
+        gam[j] = gv[j] * kLog2e;
+        asm("" : "+v"(gam[j]));  // keeps gam + dpp(gam) a DPP add (not a product folded into an fma)
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) gam[j] += dpp_move<0x111>(gam[j]);  // row_shr:1
 #pragma unroll
@@ -340,14 +345,12 @@ __device__ __forceinline__ void kside(Ops &op, f32x4 (&gr)[4][2][64], float (&bt
     for (int j = 0; j < 8; ++j) gam[j] += dpp_move<0x114>(gam[j]);  // row_shr:4
 #pragma unroll
     for (int j = 0; j < 8; ++j) gam[j] += dpp_move<0x118>(gam[j]);  // row_shr:8
-    float ep[8], em[8], eC[8];
+    float ep[8], em[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         ep[j] = __builtin_amdgcn_exp2f(gam[j]);
         em[j] = __builtin_amdgcn_exp2f(-gam[j]);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) eC[j] = row_bcast<15>(ep[j]);  // e^gamma_C of that channel
     float qb[8], kb[8], kh[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -364,11 +367,12 @@ __device__ __forceinline__ void kside(Ops &op, f32x4 (&gr)[4][2][64], float (&bt
     op.kht[2 * kw][1][lane] = transpose_tile(first4(Kh.lo), ident);
     op.kht[2 * kw + 1][0][lane] = transpose_tile(last4(Kh.hi), ident);
     op.kht[2 * kw + 1][1][lane] = transpose_tile(last4(Kh.lo), ident);
-    if (n16 == 0) {
-        // slots j < 4 of row g are channels 32 kw + 4 g + j, i.e. row half kw / 2, tile
-        // t = 2 (kw % 2), q = j; slots j >= 4 the same q in tile t + 1
+    if (n16 == kC - 1) {
+        // the last token's e^gamma is e^gamma_C.  Slots j < 4 of row g are
+        // channels 32 kw + 4 g + j, i.e. row half kw / 2, tile t = 2 (kw % 2),
+        // q = j; slots j >= 4 the same q in tile t + 1
 #pragma unroll
-        for (int q = 0; q < 4; ++q) reinterpret_cast<f32x2 *>(&op.eq[kw >> 1][grp][q])[kw & 1] = f32x2{eC[q], eC[q + 4]};
+        for (int q = 0; q < 4; ++q) reinterpret_cast<f32x2 *>(&op.eq[kw >> 1][grp][q])[kw & 1] = f32x2{ep[q], ep[q + 4]};
     }
     if (kw == 0 && grp == 0) bt[n16] = in.beta;
     // partial Grams over this quarter, transposed:
@@ -382,33 +386,27 @@ __device__ __forceinline__ void kside(Ops &op, f32x4 (&gr)[4][2][64], float (&bt
 __device__ __forceinline__ void solve(const f32x4 (&gr)[4][2][64], const float (&bt)[kC], f32x4 (&arow)[kC][5],
                                       bf16x4 (&Mo)[2][64], f32x4 (&Po)[64], int kw, int grp, int n16, int lane) {
     // lane (row r = n, column group g): sum the partial Grams of row r, columns 4g .. 4g + 3
-    f32x4 as = gr[0][0][lane], ps = gr[0][1][lane];
+    f32x4 as = gr[0][0][lane];
 #pragma unroll
-    for (int ww = 1; ww < 4; ++ww) {
-        as += gr[ww][0][lane];
-        ps += gr[ww][1][lane];
-    }
-    const float beta_r = bt[n16];
-    f32x4 av;
+    for (int ww = 1; ww < 4; ++ww) as += gr[ww][0][lane];
+    const float nbeta_r = -bt[n16];
+    f32x4 av;  // row r of -A
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        av[i] = (4 * grp + i < n16) ? beta_r * as[i] : 0.f;
-        ps[i] = (4 * grp + i <= n16) ? ps[i] : 0.f;
-    }
+    for (int i = 0; i < 4; ++i) av[i] = (4 * grp + i < n16) ? nbeta_r * as[i] : 0.f;
     arow[n16][grp] = av;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float ar[kC];  // row n of A
+    float nar[kC];  // row n of -A
 #pragma unroll
     for (int u4 = 0; u4 < 4; ++u4) {
         const f32x4 row = arow[n16][u4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ar[4 * u4 + j] = row[j];
+        for (int j = 0; j < 4; ++j) nar[4 * u4 + j] = row[j];
     }
     const int s = 4 * kw + grp;  // the column this lane solves
     float x = (n16 == s) ? 1.f : 0.f;
-    tri_pivots<0>(x, ar);
+    tri_pivots<0>(x, nar);
     // M[n][s] goes to slot s % 4 = grp of lane 16 (s / 4) + n = 16 kw + n of
     // the A operand of U = M Z, as a hi/lo bf16 pair
     const float m = x * bt[s];
@@ -416,9 +414,15 @@ __device__ __forceinline__ void solve(const f32x4 (&gr)[4][2][64], const float (
     const __bf16 ml = static_cast<__bf16>(m - static_cast<float>(mh));
     reinterpret_cast<__bf16 *>(&Mo[0][16 * kw + n16])[grp] = mh;
     reinterpret_cast<__bf16 *>(&Mo[1][16 * kw + n16])[grp] = ml;
-    // every solver wave forms the same P (same sums in the same order) and
-    // stores it (no branch on the wave index)
-    Po[lane] = ps;
+    // P (lower triangle with the diagonal) comes from solver wave 0 alone
+    if (kw == 0) {
+        f32x4 ps = gr[0][1][lane];
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) ps += gr[ww][1][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ps[i] = (4 * grp + i <= n16) ? ps[i] : 0.f;
+        Po[lane] = ps;
+    }
 }
 
 // Operands of one chunk that a state wave holds in registers.  They are read
