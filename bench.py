@@ -39,10 +39,11 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def prefill_bytes(B, T, H, D, in_bytes=2, h0=False, hT=True):
-    """Algorithmic HBM bytes of one prefill: q, k, v (in dtype), g (fp32) and
-    beta (fp32) read once, o (fp32) written once, states read/written once."""
-    per_tok_head = 3 * D * in_bytes + 4 * D + 4 + 4 * D
+def prefill_bytes(B, T, H, D, in_bytes=2, h0=False, hT=True, gate_bytes=4):
+    """Algorithmic HBM bytes of one prefill: q, k, v (in dtype), the gate (fp32
+    log-decay, or logits of gate_bytes each) and beta (fp32) read once, o (fp32)
+    written once, states read/written once."""
+    per_tok_head = 3 * D * in_bytes + gate_bytes * D + 4 + 4 * D
     state = 4 * D * D
     return B * T * H * per_tok_head + B * H * state * (int(h0) + int(hT))
 
@@ -68,8 +69,9 @@ def load_traffic(kernel="prefill"):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    sha = t.get("kernel_src_sha") if kernel == "prefill" else t.get("decode_src_sha")
-    if sha != source_hash(KERNEL_SOURCES if kernel == "prefill" else DECODE_SOURCES):
+    pre = kernel in ("prefill", "gate")  # the plain and fused-gate prefill share their sources
+    sha = t.get("kernel_src_sha") if pre else t.get("decode_src_sha")
+    if sha != source_hash(KERNEL_SOURCES if pre else DECODE_SOURCES):
         return None
     return (t.get(kernel) or {}).get("hbm_bytes_per_launch")
 
@@ -115,6 +117,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--ckpt-every", type=int, default=0,
                     help="also time the prefill that writes state checkpoints every N tokens (N a multiple of 16)")
+    ap.add_argument("--gate-logits", choices=["none", "f32", "bf16"], default="bf16",
+                    help="also time the fused gate prologue (kda_chunk_fwd_gate) with logits of this dtype")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain device copy of %d bytes first (for the traffic counters)" % (1 << 30))
     args = ap.parse_args()
@@ -139,7 +143,9 @@ def main():
 
     cfg = kda_inputs.PREFILL_64K
     log("generating %s on the device" % cfg.name)
-    x = kda_inputs.config_inputs(cfg, device=dev)
+    gate_dt = None if args.gate_logits == "none" else args.gate_logits
+    x = kda_inputs.prefill_inputs(cfg.B, cfg.T, cfg.H, cfg.D, cfg.dtype, h0=cfg.h0, seed=cfg.seed, device=dev,
+                                  gate_logits=gate_dt)
     o = torch.empty((cfg.B, cfg.T, cfg.H, cfg.D), dtype=torch.float32, device=dev)
     hT = torch.empty((cfg.B, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dev)
     dcfg = kda_inputs.DECODE_B256
@@ -214,6 +220,17 @@ def main():
         torch.cuda.synchronize()
         ck_ms = [e[0].elapsed_time(e[1]) for e in ck_ev]
         del ck
+    gate_ms = []
+    if gate_dt is not None:
+        # the fused gate prologue: the same workload with the gate given as logits
+        gate_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        kda.chunk_fwd_gate(x["q"], x["k"], x["v"], x["x"], x["beta"], None, o=o, hT=hT, stream=stream)
+        for i in range(args.steps):
+            gate_ev[i][0].record(stream)
+            kda.chunk_fwd_gate(x["q"], x["k"], x["v"], x["x"], x["beta"], None, o=o, hT=hT, stream=stream)
+            gate_ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        gate_ms = [e[0].elapsed_time(e[1]) for e in gate_ev]
     pre_ms = [e[0].elapsed_time(e[1]) for e in pre_ev]
     dec_ms = [e[0].elapsed_time(e[1]) for e in dec_ev] if d is not None else []
     pre_avg = sum(pre_ms) / len(pre_ms)
@@ -260,6 +277,15 @@ def main():
         result["checkpoints"] = {"every_tokens": args.ckpt_every, "count": n_ck, "ms": ck_avg,
                                  "overhead": ck_avg / pre_avg - 1.0, "alg_bytes_per_launch": ck_bytes,
                                  "achieved_GBps": ck_bytes / (ck_avg * 1e-3) / 1e9}
+    if gate_ms:
+        g_avg = sum(gate_ms) / len(gate_ms)
+        g_bytes = prefill_bytes(cfg.B, cfg.T, cfg.H, cfg.D, 2, h0=False, hT=True,
+                                gate_bytes=2 if gate_dt == "bf16" else 4)
+        g_ach = g_bytes / (g_avg * 1e-3) / 1e9
+        result["gate_fused"] = {"workload": cfg.name + "_gate_logits_" + gate_dt, "ms": g_avg,
+                                "vs_log_decay_entry": g_avg / pre_avg, "achieved": g_ach, "peak": HBM_PEAK_GBPS,
+                                "unit": "GB/s", "frac": g_ach / HBM_PEAK_GBPS, "alg_bytes_per_launch": g_bytes,
+                                "traffic": load_traffic("gate") if gate_dt == "bf16" else None}
     if not args.no_cpu_baseline:
         del x, o, hT
         log("cpu baseline (oracle), ~%.0f s" % args.cpu_seconds)

@@ -29,7 +29,8 @@ import sys
 
 import bench
 
-PREFILL = "prefill_mfma_kernel"
+PREFILL = "prefill_mfma_kernel<false, 0>"    # plain prefill (fp32 log-decay gate)
+GATE = "prefill_mfma_kernel<false, 2>"       # fused gate prologue, bf16 logits
 DECODE = "decode_kernel"
 COPY = "copyBuffer"
 
@@ -78,9 +79,11 @@ def main(dt, df, dw, out):
     sf, sw = kib / copy_f, kib / copy_w
     res = {"copy_bytes": bench.COPY_BYTES, "fetch_scale": sf, "write_scale": sw,
            "kernel_src_sha": bench.source_hash(), "decode_src_sha": bench.source_hash(bench.DECODE_SOURCES)}
-    for key, tag in ((PREFILL, "prefill"), (DECODE, "decode")):
+    for key, tag in ((PREFILL, "prefill"), (GATE, "gate"), (DECODE, "decode")):
         f, nf = mean_for(fetch, key)
         w, nw = mean_for(write, key)
+        if f is None or w is None:
+            continue
         res[tag] = {"fetch_kib_raw": f, "write_kib_raw": w, "dispatches": [nf, nw],
                     "fetch_bytes": f * 1024 * sf, "write_bytes": w * 1024 * sw,
                     "hbm_bytes_per_launch": f * 1024 * sf + w * 1024 * sw}
@@ -88,13 +91,15 @@ def main(dt, df, dw, out):
     stats = _csv(dt, "kernel_stats.csv")
     res["kernel_stats"] = [{"name": r["Name"][:90], "calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
                             "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])}
-                           for r in stats if PREFILL in r["Name"] or DECODE in r["Name"] or COPY in r["Name"]]
+                           for r in stats if "prefill_mfma_kernel" in r["Name"] or DECODE in r["Name"]
+                           or COPY in r["Name"]]
     os.makedirs(out, exist_ok=True)
     with open(os.path.join(out, "kda_prefill_64k_traffic.json"), "w") as f:
         json.dump(res, f, indent=1)
     alg_p = bench.prefill_bytes(1, 65536, 56, 128)
     alg_d = bench.decode_bytes(256, 56, 128)
-    lines = ["# rocprofv3: KDA prefill (B=1 H=56 T=65536 d=128) and decode (B=256 H=56 d=128)", "",
+    lines = ["# rocprofv3: KDA prefill (B=1 H=56 T=65536 d=128; fp32 log-decay gate, and bf16 gate logits with "
+             "the fused gate prologue) and decode (B=256 H=56 d=128)", "",
              "Commands (from the repository root):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d DIR_T -o trace -- "
              "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline",
@@ -113,7 +118,10 @@ def main(dt, df, dw, out):
               "scale factors %.4f (fetch), %.4f (write)." % (bench.COPY_BYTES, copy_f, copy_w, sf, sw), "",
               "| kernel | raw fetch KiB | raw write KiB | scaled bytes | algorithmic bytes | ratio |",
               "|---|---|---|---|---|---|"]
-    for tag, alg in (("prefill", alg_p), ("decode", alg_d)):
+    alg_g = bench.prefill_bytes(1, 65536, 56, 128, gate_bytes=2)
+    for tag, alg in (("prefill", alg_p), ("gate", alg_g), ("decode", alg_d)):
+        if tag not in res:
+            continue
         r = res[tag]
         lines.append("| %s | %.0f | %.0f | %.4g | %.4g | %.3f |" % (tag, r["fetch_kib_raw"], r["write_kib_raw"],
                                                                   r["hbm_bytes_per_launch"], alg,

@@ -114,6 +114,32 @@ kda_status kda_chunk_fwd_ckpt(const void *q, const void *k, const void *v,
                               kda_dtype in_dtype, float scale, void *stream);
 
 /*
+ * kda_chunk_fwd_gate -- kda_chunk_fwd with the forget gate given as its
+ * logit, turned into the log-decay inside the kernel (the gate prologue fused
+ * into the prefill):
+ *
+ *   g = g_min * sigmoid(x) = g_min / (1 + exp(-x))   per key channel,
+ *
+ * the bounded scaled-sigmoid gate with floor g_min of the Kimi K3 paper digest
+ * (devpress.csdn.net), section 2.1 (1).  Saves the separate pass that would
+ * write g, and with bf16 logits halves the gate's bytes.
+ *
+ *   x          [B, T, H, Dk] in gate_dtype (KDA_F32 or KDA_BF16): gate logits
+ *   gate_dtype storage type of x
+ *   g_min      floor of the gate, finite and -5 <= g_min < 0 (the bound the
+ *              chunk form needs); anything else is KDA_ERR_INVALID_ARGUMENT
+ *
+ * All other arguments, the layouts and the errors are those of kda_chunk_fwd
+ * (x takes the place and the alignment and overlap rules of g).
+ */
+kda_status kda_chunk_fwd_gate(const void *q, const void *k, const void *v,
+                              const void *x, kda_dtype gate_dtype, float g_min,
+                              const float *beta, const float *h0,
+                              float *o, float *hT,
+                              int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                              kda_dtype in_dtype, float scale, void *stream);
+
+/*
  * kda_decode_step -- one new token per sequence (recurrent decoding, the case
  * behind the 4x decoding speed-up at 1M tokens quoted in "Kimi K3
  * Architecture Explained", section 3): the recurrence above with T = 1,

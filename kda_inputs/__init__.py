@@ -103,15 +103,20 @@ def fill_prefill_segment(bufs: dict, t0: int, t1: int, *, seed: int, seg: int,
     bufs["beta"][:, t0:t1] = torch.sigmoid(_normal((B, n, H), seed, _TID["beta"], seg, dev))
     x = _normal((B, n, H, D), seed, _TID["gate"], seg, dev, mean=gate_mean)
     bufs["g"][:, t0:t1] = G_MIN * torch.sigmoid(x)
+    if "x" in bufs:  # the gate logits themselves, in their storage dtype
+        bufs["x"][:, t0:t1] = x.to(bufs["x"].dtype)
 
 
 def prefill_inputs(B: int, T: int, H: int, D: int, dtype: str = "bf16", *,
                    h0: bool = False, seed: int = 0, device="cpu",
-                   gate_mean: float = 0.0, Dv: int | None = None) -> dict:
+                   gate_mean: float = 0.0, Dv: int | None = None,
+                   gate_logits: str | None = None) -> dict:
     """Allocate and draw a full prefill input set.
 
     Returns a dict with q, k, v ([B, T, H, D], dtype), g ([B, T, H, D], fp32),
-    beta ([B, T, H], fp32) and h0 ([B, H, D, Dv] fp32, or None).
+    beta ([B, T, H], fp32) and h0 ([B, H, D, Dv] fp32, or None).  With
+    ``gate_logits`` ("f32" or "bf16") it also holds x, the gate logits g is
+    drawn from, stored in that dtype.
     """
     Dv = D if Dv is None else Dv
     td = torch_dtype(dtype)
@@ -122,6 +127,8 @@ def prefill_inputs(B: int, T: int, H: int, D: int, dtype: str = "bf16", *,
         "g": torch.empty((B, T, H, D), dtype=torch.float32, device=device),
         "beta": torch.empty((B, T, H), dtype=torch.float32, device=device),
     }
+    if gate_logits is not None:
+        bufs["x"] = torch.empty((B, T, H, D), dtype=torch_dtype(gate_logits), device=device)
     for seg, t0 in enumerate(range(0, T, SEGMENT)):
         fill_prefill_segment(bufs, t0, min(T, t0 + SEGMENT), seed=seed, seg=seg, gate_mean=gate_mean)
     bufs["h0"] = _normal((B, H, D, Dv), seed, _TID["h0"], 0, device, std=0.1) if h0 else None

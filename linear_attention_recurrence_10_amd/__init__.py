@@ -55,6 +55,9 @@ def library() -> ctypes.CDLL:
             lib.kda_chunk_fwd_ckpt.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, fp, i64, i64, i64, i64, i64, i64,
                                                ctypes.c_int, ctypes.c_float, vp]
             lib.kda_chunk_fwd_ckpt.restype = ctypes.c_int
+            lib.kda_chunk_fwd_gate.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_float, fp, fp, fp, fp,
+                                               i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, vp]
+            lib.kda_chunk_fwd_gate.restype = ctypes.c_int
             lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, i64, i64, i64, i64,
                                             ctypes.c_int, ctypes.c_float, vp]
             lib.kda_decode_step.restype = ctypes.c_int
@@ -83,7 +86,7 @@ def _dtype_code(t: torch.Tensor) -> int:
         return KDA_BF16
     if t.dtype == torch.float32:
         return KDA_F32
-    raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
+    raise TypeError("q, k, v and gate logits must be bfloat16 or float32, got %s" % t.dtype)
 
 
 def _ptr(t):
@@ -140,6 +143,42 @@ def chunk_fwd(q, k, v, g, beta, h0=None, *, scale: float | None = None, o=None, 
     lib = library()
     _check(lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
                              B, T, H, Dk, Dv, _dtype_code(q), float(scale or 0.0), _stream(stream)))
+    return o, hT
+
+
+def chunk_fwd_gate(q, k, v, x, beta, h0=None, *, g_min: float = -5.0, scale: float | None = None, o=None,
+                   hT=None, output_final_state: bool = True, stream=None):
+    """Chunked KDA prefill with the gate given as its logit (``kda_chunk_fwd_gate``).
+
+    x: [B, T, H, Dk] gate logits, fp32 or bf16; the kernel uses the log-decay
+    g = g_min * sigmoid(x), with -5 <= g_min < 0.  Everything else as
+    :func:`chunk_fwd`.
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(x, "x")
+    _need(beta, "beta", torch.float32)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.float32)
+    if hT is None and output_final_state:
+        hT = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if hT is not None:
+        _need(hT, "hT", torch.float32)
+    shapes_ok = (k.shape == q.shape and x.shape == q.shape and v.shape[:3] == (B, T, H)
+                 and beta.shape == (B, T, H) and o.shape == (B, T, H, Dv)
+                 and (h0 is None or h0.shape == (B, H, Dk, Dv))
+                 and (hT is None or hT.shape == (B, H, Dk, Dv)))
+    if not shapes_ok:
+        raise ValueError("inconsistent shapes")
+    lib = library()
+    _check(lib.kda_chunk_fwd_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(x), _dtype_code(x), float(g_min), _ptr(beta),
+                                  _ptr(h0), _ptr(o), _ptr(hT), B, T, H, Dk, Dv, _dtype_code(q),
+                                  float(scale or 0.0), _stream(stream)))
     return o, hT
 
 

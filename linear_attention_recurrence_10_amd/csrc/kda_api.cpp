@@ -130,9 +130,10 @@ int kda_version(void) { return 100; }  // 0.1.0
 namespace {
 
 // The prefill entry points: kda_chunk_fwd is this with no checkpoints.
-kda_status chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                     const float *h0, float *o, float *hT, float *ckpt, int64_t ckpt_every, int64_t B, int64_t T,
-                     int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale, void *stream) {
+kda_status chunk_fwd(const void *q, const void *k, const void *v, const void *g, kda::GateMode gate, float g_min,
+                     const float *beta, const float *h0, float *o, float *hT, float *ckpt, int64_t ckpt_every,
+                     int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale,
+                     void *stream) {
     if (B <= 0 || H <= 0 || Dk <= 0 || Dv <= 0 || T < 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "sizes must be positive (T >= 0): B=%lld T=%lld H=%lld Dk=%lld Dv=%lld",
                     (long long)B, (long long)T, (long long)H, (long long)Dk, (long long)Dv);
@@ -162,8 +163,9 @@ kda_status chunk_fwd(const void *q, const void *k, const void *v, const float *g
         return fail(KDA_ERR_INVALID_ARGUMENT, "tensor sizes overflow 64 bits");
     const uint64_t esz = in_dtype == KDA_BF16 ? 2 : 4;
 
+    const uint64_t gsz = gate == kda::kGateLogitBf16 ? 2 : 4;
     const Span sp[] = {
-        {"q", q, n_qk * esz}, {"k", k, n_qk * esz},    {"v", v, n_v * esz},         {"g", g, n_qk * 4},
+        {"q", q, n_qk * esz}, {"k", k, n_qk * esz},    {"v", v, n_v * esz},         {"g", g, n_qk * gsz},
         {"beta", beta, n_tok * 4}, {"h0", h0, n_state * 4}, {"o", o, n_v * 4}, {"hT", hT, n_state * 4},
         {"ckpt", n_ckpt > 0 ? ckpt : nullptr, n_ck * 4},
     };
@@ -187,6 +189,8 @@ kda_status chunk_fwd(const void *q, const void *k, const void *v, const float *g
 
     kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.hT = hT;
+    a.gate = gate;
+    a.g_min = g_min;
     a.ckpt = n_ckpt > 0 ? ckpt : nullptr;
     a.ckpt_every = ckpt ? ckpt_every / kda::kChunk : 0;
     a.n_ckpt = n_ckpt;
@@ -206,14 +210,29 @@ extern "C" {
 kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
                          const float *h0, float *o, float *hT, int64_t B, int64_t T, int64_t H, int64_t Dk,
                          int64_t Dv, kda_dtype in_dtype, float scale, void *stream) {
-    return chunk_fwd(q, k, v, g, beta, h0, o, hT, nullptr, 0, B, T, H, Dk, Dv, in_dtype, scale, stream);
+    return chunk_fwd(q, k, v, g, kda::kGateLogDecay, 0.f, beta, h0, o, hT, nullptr, 0, B, T, H, Dk, Dv, in_dtype,
+                     scale, stream);
 }
 
 kda_status kda_chunk_fwd_ckpt(const void *q, const void *k, const void *v, const float *g, const float *beta,
                               const float *h0, float *o, float *hT, float *ckpt, int64_t ckpt_every, int64_t B,
                               int64_t T, int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale,
                               void *stream) {
-    return chunk_fwd(q, k, v, g, beta, h0, o, hT, ckpt, ckpt_every, B, T, H, Dk, Dv, in_dtype, scale, stream);
+    return chunk_fwd(q, k, v, g, kda::kGateLogDecay, 0.f, beta, h0, o, hT, ckpt, ckpt_every, B, T, H, Dk, Dv,
+                     in_dtype, scale, stream);
+}
+
+kda_status kda_chunk_fwd_gate(const void *q, const void *k, const void *v, const void *x, kda_dtype gate_dtype,
+                              float g_min, const float *beta, const float *h0, float *o, float *hT, int64_t B,
+                              int64_t T, int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale,
+                              void *stream) {
+    if (gate_dtype != KDA_F32 && gate_dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown gate_dtype %d", static_cast<int>(gate_dtype));
+    if (!(g_min >= -5.f && g_min < 0.f))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "g_min=%g must satisfy -5 <= g_min < 0", static_cast<double>(g_min));
+    const kda::GateMode gate = gate_dtype == KDA_BF16 ? kda::kGateLogitBf16 : kda::kGateLogitF32;
+    return chunk_fwd(q, k, v, x, gate, g_min, beta, h0, o, hT, nullptr, 0, B, T, H, Dk, Dv, in_dtype, scale,
+                     stream);
 }
 
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,

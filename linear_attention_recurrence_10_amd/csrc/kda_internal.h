@@ -8,9 +8,15 @@ namespace kda {
 
 constexpr int kChunk = 16;  // tokens per chunk: g_min = -5 keeps exp(+-16*5) inside bf16 range
 
+// How the per-channel forget gate is given: the fp32 log-decay g itself, or
+// its logit x (fp32 or bf16) with g = g_min * sigmoid(x) formed in the kernel.
+enum GateMode { kGateLogDecay = 0, kGateLogitF32 = 1, kGateLogitBf16 = 2 };
+
 struct PrefillArgs {
     const void *q, *k, *v;   // [B,T,H,D] in dtype
-    const float *g;          // [B,T,H,D]
+    const void *g;           // [B,T,H,D]: fp32 log-decay, or logits (gate)
+    int gate;                // GateMode
+    float g_min;             // floor of the gate for the logit modes
     const float *beta;       // [B,T,H]
     const float *h0;         // [B,H,D,D] or null
     float *o;                // [B,T,H,D]
@@ -41,6 +47,14 @@ hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s);
 bool prefill_mfma_supported(const PrefillArgs &a);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+
+// g = g_min * sigmoid(x) = g_min / (1 + e^-x): the bounded scaled-sigmoid
+// gate of the Kimi K3 paper digest (devpress.csdn.net), section 2.1 (1), with
+// the hardware exp2 and reciprocal (about 1 ulp each).  x -> -inf gives 0,
+// x -> +inf gives g_min.
+__device__ __forceinline__ float gate_of_logit(float x, float g_min) {
+    return g_min * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
 
 // bf16 (stored as raw 16-bit patterns) and fp32 element loads.
 __device__ __forceinline__ float ld_elem(const uint16_t *p, int64_t i) {

@@ -229,7 +229,8 @@ struct Smem {
 // and beta of token n.
 struct KRaw {
     u32x2 q[2], k[2];
-    f32x4 g[2];
+    f32x4 g[2];   // fp32 log-decay or fp32 logits
+    u32x2 gx[2];  // bf16 logits
     float beta;
 };
 
@@ -246,6 +247,7 @@ __device__ __forceinline__ KOff kraw_offsets(const PrefillArgs &a, int tok, int 
     const int HD = static_cast<int>(a.H) * kD;
     return KOff{static_cast<uint32_t>(tok * HD + 32 * kw + 4 * grp), static_cast<uint32_t>(tok * static_cast<int>(a.H))};
 }
+template <int G>  // GateMode
 __device__ __forceinline__ void load_kraw(KRaw &r, const PrefillArgs &a, int64_t t0, int64_t b, int64_t h, int kw,
                                           int grp, int n16, const KOff &full) {
     const int64_t T = a.T, H = a.H;
@@ -253,7 +255,7 @@ __device__ __forceinline__ void load_kraw(KRaw &r, const PrefillArgs &a, int64_t
     KOff off = full;
     if (t0 + kC > T) off = kraw_offsets(a, min(n16, static_cast<int>(T - t0) - 1), kw, grp);
     const uint32_t e0 = off.tok;
-    const char *gb = reinterpret_cast<const char *>(a.g + row0 * kD);
+    const char *gb = reinterpret_cast<const char *>(a.g) + (G == kGateLogitBf16 ? 2 : 4) * (row0 * kD);
     const char *qb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.q) + row0 * kD);
     const char *kb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k) + row0 * kD);
 #pragma unroll
@@ -261,7 +263,10 @@ __device__ __forceinline__ void load_kraw(KRaw &r, const PrefillArgs &a, int64_t
         const uint32_t e = e0 + 16u * tt;
         r.q[tt] = *reinterpret_cast<const u32x2 *>(qb + 2u * e);
         r.k[tt] = *reinterpret_cast<const u32x2 *>(kb + 2u * e);
-        r.g[tt] = *reinterpret_cast<const f32x4 *>(gb + 4u * e);
+        if constexpr (G == kGateLogitBf16)
+            r.gx[tt] = *reinterpret_cast<const u32x2 *>(gb + 2u * e);
+        else
+            r.g[tt] = *reinterpret_cast<const f32x4 *>(gb + 4u * e);
     }
     r.beta = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(a.beta + row0) + 4u * off.beta);
 }
@@ -296,12 +301,23 @@ struct KIn {
 // Tokens past the end of the sequence become identity steps: their gate is
 // set to 0 and their beta to 0.  That zeroes their rows and columns of A and
 // M, hence their rows of U, so their (finite) q, k and v never contribute.
+// With gate logits, the log-decay g = g_min sigmoid(x) is formed here.
+template <int G>  // GateMode
 __device__ __forceinline__ void kside_in(const PrefillArgs &a, const KRaw &raw, KIn &in, int64_t t0, int n16) {
     in.beta = raw.beta;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) in.g[4 * tt + i] = raw.g[tt][i];
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (G == kGateLogDecay) {
+                in.g[4 * tt + i] = raw.g[tt][i];
+            } else if constexpr (G == kGateLogitF32) {
+                in.g[4 * tt + i] = gate_of_logit(raw.g[tt][i], a.g_min);
+            } else {
+                const uint32_t p = raw.gx[tt][i >> 1];
+                in.g[4 * tt + i] = gate_of_logit((i & 1) ? bf16_hi(p) : bf16_lo(p), a.g_min);
+            }
+        }
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const uint32_t qp = raw.q[tt][p], kp = raw.k[tt][p];
@@ -602,7 +618,7 @@ __device__ __forceinline__ void run_steps(int64_t nchunks, Body &&body) {
 
 // CKPT: the launch writes state checkpoints (a separate instantiation, so the
 // plain prefill carries no test for it).
-template <bool CKPT>
+template <bool CKPT, int G>  // G: GateMode
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     __shared__ Smem sm;
 
@@ -648,8 +664,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) ident[i] = static_cast<__bf16>((4 * grp + i == n16) ? 1.f : 0.f);
         if (nchunks > 0) {
-            load_kraw(raw[0], a, 0, b, h, kw, grp, n16, koff);
-            load_kraw(raw[1], a, nchunks > 1 ? kC : 0, b, h, kw, grp, n16, koff);
+            load_kraw<G>(raw[0], a, 0, b, h, kw, grp, n16, koff);
+            load_kraw<G>(raw[1], a, nchunks > 1 ? kC : 0, b, h, kw, grp, n16, koff);
         }
     } else if (swave) {
 #pragma unroll
@@ -678,10 +694,10 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             constexpr int PAR = decltype(par_tag)::value;  // n & 1
             // reload the raw buffer at the end, once the unpacked values are dead
             KIn in;
-            if constexpr (decltype(kside_tag)::value) kside_in(a, raw[PAR], in, (n + 2) * kC, n16);
+            if constexpr (decltype(kside_tag)::value) kside_in<G>(a, raw[PAR], in, (n + 2) * kC, n16);
             if constexpr (decltype(kside_tag)::value) {
                 kside(sm.ops[kslot], sm.gram[PAR], sm.beta[PAR], in, kw, grp, n16, lane, ident);
-                load_kraw(raw[PAR], a, min((n + 4) * kC, last_t0), b, h, kw, grp, n16, koff);
+                load_kraw<G>(raw[PAR], a, min((n + 4) * kC, last_t0), b, h, kw, grp, n16, koff);
             }
             kslot = (kslot == kRing - 1) ? 0 : kslot + 1;
         });
@@ -755,10 +771,17 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
     const int64_t BH = a.B * a.H;
     const int64_t rounds = (BH + 7) / 8;
     const dim3 grid(static_cast<unsigned>(rounds * 8 * kNV));
+    // checkpoints are written with the fp32 log-decay gate only (the entry
+    // points offer no other combination)
+    if (a.ckpt && a.gate != kGateLogDecay) return hipErrorInvalidValue;
     if (a.ckpt)
-        hipLaunchKernelGGL(prefill_mfma_kernel<true>, grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((prefill_mfma_kernel<true, kGateLogDecay>), grid, dim3(kThreads), 0, s, a);
+    else if (a.gate == kGateLogitF32)
+        hipLaunchKernelGGL((prefill_mfma_kernel<false, kGateLogitF32>), grid, dim3(kThreads), 0, s, a);
+    else if (a.gate == kGateLogitBf16)
+        hipLaunchKernelGGL((prefill_mfma_kernel<false, kGateLogitBf16>), grid, dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(prefill_mfma_kernel<false>, grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((prefill_mfma_kernel<false, kGateLogDecay>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -81,7 +81,12 @@ __global__ __launch_bounds__(DVS *RG) void prefill_valu_kernel(PrefillArgs a) {
                 const int64_t idx = ((b * T + t) * H + h) * D + i;
                 qv = ld_elem(q, idx);
                 kv = ld_elem(k, idx);
-                gv = a.g[idx];
+                if (a.gate == kGateLogDecay)
+                    gv = static_cast<const float *>(a.g)[idx];
+                else if (a.gate == kGateLogitF32)
+                    gv = gate_of_logit(static_cast<const float *>(a.g)[idx], a.g_min);
+                else
+                    gv = gate_of_logit(ld_elem(static_cast<const uint16_t *>(a.g), idx), a.g_min);
             }
             sQ[r][i] = qv;
             sKh[r][i] = kv;

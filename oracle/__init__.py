@@ -79,6 +79,21 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
+def gate_from_logit(x, g_min: float = -5.0) -> np.ndarray:
+    """Per-channel log-decay from the gate logit, in fp64:
+    ``g = g_min * sigmoid(x) = g_min / (1 + exp(-x))``.
+
+    The bounded scaled-sigmoid gate with floor ``g_min`` of the Kimi K3 paper
+    digest (devpress.csdn.net), section 2.1 (1) ("数值稳定优化"): the gate is
+    kept in (g_min, 0) so that the in-chunk reciprocal factors stay in range.
+    ``x`` is taken exactly as stored (bf16 or fp32 converted to fp64).
+    """
+    x = _f64(x.float().cpu().numpy() if hasattr(x, "float") else x)
+    # exp(-x) overflows to inf for x < -709: the quotient is then 0, the limit
+    with np.errstate(over="ignore"):
+        return g_min / (1.0 + np.exp(-x))
+
+
 def kda_fwd(q, k, v, g, beta, h0=None, scale=None):
     """Token-sequential KDA forward in fp64 (C implementation).
 

@@ -151,3 +151,28 @@ def test_ckpt_null_ignores_interval(lib):
     ptrs[0] = None    # then the first error is the null input, not the interval
     assert chunk_ckpt(lib, every=7, ptrs=ptrs) == 1
     assert b"non-null" in lib.kda_last_error()
+
+
+def chunk_gate(lib, g_min=-5.0, gate_dtype=1, T=64, ptrs=None):
+    p = ptrs or [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(8)]
+    return lib.kda_chunk_fwd_gate(p[0], p[1], p[2], p[3], gate_dtype, g_min, p[4], p[5], p[6], p[7],
+                                  1, T, 1, 128, 128, 1, 0.0, None)
+
+
+@pytest.mark.parametrize("g_min", [0.0, 0.5, -5.5, -100.0, float("nan"), float("-inf")])
+def test_gate_floor_out_of_range(lib, g_min):
+    assert chunk_gate(lib, g_min=g_min) == 1
+    assert b"g_min" in lib.kda_last_error()
+
+
+def test_gate_dtype_must_be_known(lib):
+    assert chunk_gate(lib, gate_dtype=5) == 1
+    assert b"gate_dtype" in lib.kda_last_error()
+
+
+def test_gate_shares_the_prefill_checks(lib):
+    assert chunk_gate(lib, T=-1) == 1
+    ptrs = [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(8)]
+    ptrs[6] = ctypes.c_void_p(ptrs[3].value + 64)   # o inside the logits
+    assert chunk_gate(lib, ptrs=ptrs) == 1
+    assert b"o overlaps g" in lib.kda_last_error()

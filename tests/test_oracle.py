@@ -154,3 +154,47 @@ def test_planted_mistake_is_caught(kind):
         except Exception:  # AssertionError or a shape error from the broken code
             failed.append(pin.__name__)
     assert failed, "mutant %s passed every pin" % kind
+
+
+# ---- the gate prologue: g = g_min * sigmoid(x) (Kimi K3 paper digest, section 2.1 (1)) ----
+
+def test_gate_closed_forms():
+    gm = -5.0
+    g = oracle.gate_from_logit(np.array([0.0, 800.0, -800.0, np.log(3.0)]), gm)
+    assert g[0] == gm / 2                       # sigmoid(0) = 1/2
+    assert g[1] == gm and g[2] == 0.0           # the two limits, with no overflow to nan
+    assert abs(g[3] - gm * 0.75) < 1e-15        # sigmoid(ln 3) = 3/4
+
+
+def test_gate_symmetry_and_monotone():
+    x = np.linspace(-30.0, 30.0, 2001)
+    for gm in (-5.0, -1.0, -0.25):
+        g = oracle.gate_from_logit(x, gm)
+        # sigmoid(x) + sigmoid(-x) = 1
+        assert np.max(np.abs(g + oracle.gate_from_logit(-x, gm) - gm)) < 1e-14
+        assert np.all(np.diff(g) < 0) or np.all(np.diff(g) <= 0)  # decreasing (g_min < 0)
+        assert np.all((g <= 0) & (g >= gm))
+
+
+def test_gate_matches_library_sigmoid():
+    from scipy.special import expit
+
+    x = np.random.default_rng(5).normal(0.0, 3.0, size=10000)
+    for gm in (-5.0, -2.5):
+        # a few ulp of |g| <= 5 (the two routines round in a different order)
+        assert np.max(np.abs(oracle.gate_from_logit(x, gm) - gm * expit(x))) < 8 * np.finfo(float).eps * abs(gm)
+
+
+def test_gate_slope_at_zero():
+    # d/dx [g_min sigmoid(x)] at 0 is g_min / 4
+    h = 1e-6
+    d = (oracle.gate_from_logit(np.array([h]), -5.0) - oracle.gate_from_logit(np.array([-h]), -5.0)) / (2 * h)
+    assert abs(d[0] - (-5.0 / 4)) < 1e-8
+
+
+def test_gate_takes_bf16_logits_as_stored():
+    import torch
+
+    x = torch.tensor([0.1, -1.7, 3.3], dtype=torch.bfloat16)
+    xs = x.float().double().numpy()  # the stored bf16 values, exactly
+    assert np.array_equal(oracle.gate_from_logit(x, -5.0), -5.0 / (1.0 + np.exp(-xs)))
