@@ -59,9 +59,9 @@
 // slots.  q, k, g are loaded straight into it with 8- and 16-byte loads, and
 // the cumulative decay over tokens is a prefix sum across the 16 lanes of a
 // row (DPP row shifts).  Kh in the update, a contraction over tokens, needs
-// "channel per lane" (channel n, tokens 4g .. 4g + 3): a 16x16x16 product
-// with the identity converts it exactly (its inputs are bf16).  The
-// Grams are formed transposed (Kh Kb^T, Kh Qb^T), so their result layout is
+// "channel per lane" (channel n, tokens 4g .. 4g + 3): the k-side stores its
+// tiles token-major and the state waves read them with gfx950's transposing
+// LDS read, which delivers that layout.  The Grams are formed transposed (Kh Kb^T, Kh Qb^T), so their result layout is
 // "row n, columns 4g + i", the A-operand layout of U = M Z and P U.
 #include <cstdlib>
 #include <type_traits>
@@ -162,17 +162,7 @@ __device__ __forceinline__ f32x4 mm16(const Sp4 &a, const Sp4 &b, f32x4 c) {
     return c;
 }
 
-// bf16 values (exact) from an fp32 result vector.
-__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
-    const bf16x2 a = __builtin_convertvector((f32x2){x[0], x[1]}, bf16x2);
-    const bf16x2 b = __builtin_convertvector((f32x2){x[2], x[3]}, bf16x2);
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3);
-}
 
-// "token per lane" -> "channel per lane" for one 16x16 bf16 tile, exact.
-__device__ __forceinline__ bf16x4 transpose_tile(bf16x4 x, bf16x4 ident) {
-    return to_bf16x4(mfma16(x, ident, f32x4{0.f, 0.f, 0.f, 0.f}));
-}
 
 __device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
@@ -209,7 +199,7 @@ __device__ __forceinline__ void tri_pivots(float &x, const float (&nar)[kC]) {
 // it (every access is lane-contiguous): one slot of the LDS ring.
 struct Ops {
     bf16x8 qk[2][4][2][64];  // [Qb, Kb][32-channel quarter][hi, lo][lane], token per lane
-    bf16x4 kht[8][2][64];    // [16-channel tile][hi, lo][lane], Kh channel per lane
+    bf16x4 kht[8][2][64];    // [16-channel tile][hi, lo][4 token + channel / 4], Kh token-major
     f32x4 eq[2][4][4];       // e^gamma_C: [rh][g][q] holds channels 64 rh + 16 t + 4 g + q, t = 0..3
     bf16x4 Mhl[2][64];       // M = (I + A)^-1 diag(beta), split [hi, lo][lane], A-operand layout
     f32x4 P[64];             // P: lane (n, g) holds row n, columns 4g .. 4g + 3
@@ -339,7 +329,7 @@ __device__ __forceinline__ void kside_in(const PrefillArgs &a, const KRaw &raw, 
 // K-side, second part: this quarter's operands of the chunk go to `op` (LDS or
 // a shared slot in global memory), its partial Grams to `gr`, beta to `bt`.
 __device__ __forceinline__ void kside(Ops &op, f32x4 (&gr)[4][2][64], float (&bt)[kC], const KIn &in, int kw,
-                                      int grp, int n16, int lane, const bf16x4 &ident) {
+                                      int grp, int n16, int lane) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const float(&gv)[8] = in.g;
     const float(&qv)[8] = in.q;
@@ -379,10 +369,12 @@ __device__ __forceinline__ void kside(Ops &op, f32x4 (&gr)[4][2][64], float (&bt
     op.qk[0][kw][1][lane] = Qb.lo;
     op.qk[1][kw][0][lane] = Kb.hi;
     op.qk[1][kw][1][lane] = Kb.lo;
-    op.kht[2 * kw][0][lane] = transpose_tile(first4(Kh.hi), ident);
-    op.kht[2 * kw][1][lane] = transpose_tile(first4(Kh.lo), ident);
-    op.kht[2 * kw + 1][0][lane] = transpose_tile(last4(Kh.hi), ident);
-    op.kht[2 * kw + 1][1][lane] = transpose_tile(last4(Kh.lo), ident);
+    // Kh tiles token-major: token n, channels 4g .. 4g + 3 of the tile at
+    // 8-byte index 4n + g (the state waves transpose them as they read them)
+    op.kht[2 * kw][0][4 * n16 + grp] = first4(Kh.hi);
+    op.kht[2 * kw][1][4 * n16 + grp] = first4(Kh.lo);
+    op.kht[2 * kw + 1][0][4 * n16 + grp] = last4(Kh.hi);
+    op.kht[2 * kw + 1][1][4 * n16 + grp] = last4(Kh.lo);
     if (n16 == kC - 1) {
         // the last token's e^gamma is e^gamma_C.  Slots j < 4 of row g are
         // channels 32 kw + 4 g + j, i.e. row half kw / 2, tile t = 2 (kw % 2),
@@ -458,9 +450,19 @@ __device__ __forceinline__ void read_kq(SOps &s, const Ops &op, int rh, int lane
         s.Qb[js] = Sp8{op.qk[0][2 * rh + js][0][lane], op.qk[0][2 * rh + js][1][lane]};
     }
 }
+// Transposing LDS read (gfx950): inside each group of 16 lanes, lane i
+// receives in slot k the element (i mod 4) of the 8 bytes addressed by lane
+// i / 4 + 4 k.  Over a token-major 16 x 16 tile (token r, channel c at element
+// 16 r + c), with every lane addressing its own 8-byte index, lane (n, g)
+// receives channel n of tokens 4g .. 4g + 3: the A operand of Kh^T U.
+__device__ __forceinline__ bf16x4 read_tr(const bf16x4 *p) {
+    using lds_s16x4 = __attribute__((address_space(3))) s16x4;
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p)));
+}
 __device__ __forceinline__ void read_kh(SOps &s, const Ops &op, int rh, int grp, int n16, int lane) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) s.KhT[t] = Sp4{op.kht[4 * rh + t][0][lane], op.kht[4 * rh + t][1][lane]};
+    for (int t = 0; t < 4; ++t)
+        s.KhT[t] = Sp4{read_tr(&op.kht[4 * rh + t][0][lane]), read_tr(&op.kht[4 * rh + t][1][lane])};
     s.eq = op.eq[rh][grp][n16 & 3];
 }
 // lane I of each group of four lanes, to the whole group (DPP quad_perm [I, I, I, I])
@@ -652,7 +654,6 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
 
     if (tid < 4) (&sm.flag[0][0])[tid] = 0u;
 
-    bf16x4 ident;  // identity operand of the layout transposes: B[k = 4g + i][col = n] = (4g + i == n)
     const KOff koff = kraw_offsets(a, n16, kw, grp);
     uint32_t voff[4];
 #pragma unroll
@@ -661,8 +662,6 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     f32x4 S[4];  // state rows 64 rh + 16 t + 4 g + i, column `col`
     uint16_t vraw[2][4];
     if (kwave) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ident[i] = static_cast<__bf16>((4 * grp + i == n16) ? 1.f : 0.f);
         if (nchunks > 0) {
             load_kraw<G>(raw[0], a, 0, b, h, kw, grp, n16, koff);
             load_kraw<G>(raw[1], a, nchunks > 1 ? kC : 0, b, h, kw, grp, n16, koff);
@@ -696,7 +695,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             KIn in;
             if constexpr (decltype(kside_tag)::value) kside_in<G>(a, raw[PAR], in, (n + 2) * kC, n16);
             if constexpr (decltype(kside_tag)::value) {
-                kside(sm.ops[kslot], sm.gram[PAR], sm.beta[PAR], in, kw, grp, n16, lane, ident);
+                kside(sm.ops[kslot], sm.gram[PAR], sm.beta[PAR], in, kw, grp, n16, lane);
                 load_kraw<G>(raw[PAR], a, min((n + 4) * kC, last_t0), b, h, kw, grp, n16, koff);
             }
             kslot = (kslot == kRing - 1) ? 0 : kslot + 1;
