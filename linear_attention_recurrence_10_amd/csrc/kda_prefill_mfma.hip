@@ -202,7 +202,7 @@ struct Ops {
     bf16x4 kht[8][2][64];    // [16-channel tile][hi, lo][4 token + channel / 4], Kh token-major
     f32x4 eq[2][4][4];       // e^gamma_C: [rh][g][q] holds channels 64 rh + 16 t + 4 g + q, t = 0..3
     bf16x4 Mhl[2][64];       // M = (I + A)^-1 diag(beta), split [hi, lo][lane], A-operand layout
-    f32x4 P[64];             // P: lane (n, g) holds row n, columns 4g .. 4g + 3
+    bf16x4 P[2][64];         // P split [hi, lo][lane]: lane (n, g) holds row n, columns 4g .. 4g + 3
 };
 
 struct Smem {
@@ -392,7 +392,8 @@ __device__ __forceinline__ void kside(Ops &op, f32x4 (&gr)[4][2][64], float (&bt
 // M = (I + A)^-1 diag(beta) and P of the chunk whose Grams sit in the `par`
 // buffers: solver wave kw solves columns 4 kw .. 4 kw + 3, one per 16-lane row.
 __device__ __forceinline__ void solve(const f32x4 (&gr)[4][2][64], const float (&bt)[kC], f32x4 (&arow)[kC][5],
-                                      bf16x4 (&Mo)[2][64], f32x4 (&Po)[64], int kw, int grp, int n16, int lane) {
+                                      bf16x4 (&Mo)[2][64], bf16x4 (&Po)[2][64], int kw, int grp, int n16,
+                                      int lane) {
     // lane (row r = n, column group g): sum the partial Grams of row r, columns 4g .. 4g + 3
     f32x4 as = gr[0][0][lane];
 #pragma unroll
@@ -429,7 +430,9 @@ __device__ __forceinline__ void solve(const f32x4 (&gr)[4][2][64], const float (
         for (int ww = 1; ww < 4; ++ww) ps += gr[ww][1][lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ps[i] = (4 * grp + i <= n16) ? ps[i] : 0.f;
-        Po[lane] = ps;
+        const Sp4 pp = split4(ps);  // stored split: the state waves use it as is
+        Po[0][lane] = pp.hi;
+        Po[1][lane] = pp.lo;
     }
 }
 
@@ -481,7 +484,7 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
                                             int lane, const uint32_t (&voff)[4]) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const Sp4 Mf = Sp4{op.Mhl[0][lane], op.Mhl[1][lane]};
-    const f32x4 Prow = op.P[lane];
+    const Sp4 Pf = Sp4{op.P[0][lane], op.P[1][lane]};
 
     // partial X = Kb S0 and Y = Qb S0 over this wave's 64 channels; the state
     // rows of tiles 2js, 2js + 1 are the channels of operand slots 0..3, 4..7
@@ -522,7 +525,7 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
     const Sp4 U = split4(mm16(Mf, split4(vv - X), zero));
 
     if (rh == 0) {
-        const f32x4 O = mm16(split4(Prow), U, Y + Yo);
+        const f32x4 O = mm16(Pf, U, Y + Yo);
         // o has the layout of v: token 4g + i, column `col` at element offset voff[i]
         char *ob = reinterpret_cast<char *>(a.o + ((b * a.T + t0) * a.H + h) * kD);  // wave uniform
         if (t0 + kC <= a.T) {
