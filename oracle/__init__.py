@@ -11,6 +11,9 @@ Two implementations of the same token-by-token recurrence live here:
 * ``ref_numpy.py``: the same recurrence in numpy, vectorised over (b, h), used
   to cross-check the C code on small inputs.
 
+``kcp.py`` adds the segment-parallel form of the same forward pass (per-segment
+transition matrices and zero-start states, reassembled by a scan).
+
 The recurrence follows the prose of "Kimi K3 Architecture Explained", section 3
 "Kimi Delta Attention (KDA)" (decay stale context first, then erase, then
 write; DeltaNet's eraser recalls with the incoming key and writes only the
