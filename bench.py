@@ -11,6 +11,8 @@ Prints ONE JSON line on stdout:
   value          prefill tokens/s (B*T / mean prefill kernel time)
   roofline       the prefill kernel against the HBM roofline (algorithmic bytes)
   decode         the decode kernel's algorithmic GB/s against the HBM peak
+  segmented      the segmented prefill (kda_chunk_fwd_kcp) beside the single
+                 pass on one long sequence with 7 heads (B=1, T=262144)
   cpu_baseline   the fp64 oracle on the host cores, on a bounded token sample
 """
 from __future__ import annotations
@@ -107,6 +109,48 @@ def cpu_baseline(target_s: float):
     }
 
 
+def time_segmented(kda, torch, stream, n_seg, steps, single=True):
+    """The segmented prefill against the single pass (unless not `single`) on
+    one long sequence with few heads (its own inputs, freed before returning)."""
+    import kda_inputs
+
+    cfg = kda_inputs.PREFILL_256K_H7
+    dev = torch.device("cuda:0")
+    log("segmented prefill: %s, %d segments" % (cfg.name, n_seg))
+    x = kda_inputs.prefill_inputs(cfg.B, cfg.T, cfg.H, cfg.D, cfg.dtype, h0=cfg.h0, seed=cfg.seed, device=dev)
+    o = torch.empty((cfg.B, cfg.T, cfg.H, cfg.D), dtype=torch.float32, device=dev)
+    hT = torch.empty((cfg.B, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, kda.kcp_ws_bytes(cfg.B, cfg.T, cfg.H, cfg.D, cfg.D, n_seg)), dtype=torch.uint8,
+                     device=dev)
+
+    def single_pass():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], None, o=o, hT=hT, stream=stream)
+
+    def split():
+        kda.chunk_fwd_kcp(x["q"], x["k"], x["v"], x["g"], x["beta"], None, n_seg=n_seg, ws=ws, o=o, hT=hT,
+                          stream=stream)
+
+    out = {"single_pass": None}
+    runs = (("single_pass", single_pass), ("segmented", split)) if single else (("segmented", split),)
+    for name, fn in runs:
+        fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for e in ev:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        ms = [e[0].elapsed_time(e[1]) for e in ev]
+        out[name] = sum(ms) / len(ms)
+    del x, o, hT, ws
+    torch.cuda.empty_cache()
+    tokens = cfg.B * cfg.T
+    sp = out["single_pass"]
+    return {"workload": cfg.name, "n_seg": n_seg, "ms": out["segmented"], "single_pass_ms": sp,
+            "tokens_per_s": tokens / (out["segmented"] * 1e-3), "speedup": sp / out["segmented"] if sp else None,
+            "unit": "tokens/s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +163,11 @@ def main():
                     help="also time the prefill that writes state checkpoints every N tokens (N a multiple of 16)")
     ap.add_argument("--gate-logits", choices=["none", "f32", "bf16"], default="bf16",
                     help="also time the fused gate prologue (kda_chunk_fwd_gate) with logits of this dtype")
+    ap.add_argument("--segments", type=int, default=8,
+                    help="also time the segmented prefill (kda_chunk_fwd_kcp) with this many segments on one "
+                         "long 7-head sequence, beside the single pass (0 = skip)")
+    ap.add_argument("--segmented-only", action="store_true",
+                    help="time only the segmented prefill (for a kernel trace of its launches alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain device copy of %d bytes first (for the traffic counters)" % (1 << 30))
     args = ap.parse_args()
@@ -140,6 +189,15 @@ def main():
     kda.library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.segmented_only:
+        n_seg = args.segments if args.segments > 0 else 8
+        seg = time_segmented(kda, torch, torch.cuda.current_stream(), n_seg, args.steps, single=False)
+        print(json.dumps({"metric": "KDA segmented prefill tokens/s", "value": seg["tokens_per_s"],
+                          "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": 1,
+                          "ms_per_step": seg["ms"], "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+                          "config": {"workload": seg["workload"], "n_seg": n_seg}, "segmented": seg}), flush=True)
+        return
 
     cfg = kda_inputs.PREFILL_64K
     log("generating %s on the device" % cfg.name)
@@ -231,6 +289,9 @@ def main():
             gate_ev[i][1].record(stream)
         torch.cuda.synchronize()
         gate_ms = [e[0].elapsed_time(e[1]) for e in gate_ev]
+    seg = None
+    if args.segments > 0:
+        seg = time_segmented(kda, torch, stream, args.segments, args.steps)
     pre_ms = [e[0].elapsed_time(e[1]) for e in pre_ev]
     dec_ms = [e[0].elapsed_time(e[1]) for e in dec_ev] if d is not None else []
     pre_avg = sum(pre_ms) / len(pre_ms)
@@ -286,6 +347,8 @@ def main():
                                 "vs_log_decay_entry": g_avg / pre_avg, "achieved": g_ach, "peak": HBM_PEAK_GBPS,
                                 "unit": "GB/s", "frac": g_ach / HBM_PEAK_GBPS, "alg_bytes_per_launch": g_bytes,
                                 "traffic": load_traffic("gate") if gate_dt == "bf16" else None}
+    if seg is not None:
+        result["segmented"] = seg
     if not args.no_cpu_baseline:
         del x, o, hT
         log("cpu baseline (oracle), ~%.0f s" % args.cpu_seconds)

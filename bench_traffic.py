@@ -4,11 +4,11 @@ Inputs are three rocprofv3 output directories made with the commands below
 (each one a separate run; counters never share a run with other tracing):
 
   rocprofv3 --kernel-trace --stats --output-format csv -d DIR_T -o trace -- \\
-      python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline
+      python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --segments 0
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR_F -o fetch -- \\
-      python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration
+      python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --copy-calibration
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR_W -o write -- \\
-      python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration
+      python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --copy-calibration
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
 counter reads for the runtime's plain copy of COPY_BYTES bytes, so that a
@@ -17,6 +17,8 @@ OUT/kda_prefill_64k_traffic.json (read by bench.py while the kernel sources
 are unchanged) and OUT/kda_prefill_64k_decode_b256_rocprof.md.
 
 usage: python3 bench_traffic.py DIR_T DIR_F DIR_W OUT
+       python3 bench_traffic.py --segmented N_SEG DIR_T OUT   (trace summary of
+           bench.py --segmented-only: OUT/kda_prefill_256k_h7_segmented_rocprof.md)
 """
 from __future__ import annotations
 
@@ -29,8 +31,8 @@ import sys
 
 import bench
 
-PREFILL = "prefill_mfma_kernel<false, 0>"    # plain prefill (fp32 log-decay gate)
-GATE = "prefill_mfma_kernel<false, 2>"       # fused gate prologue, bf16 logits
+PREFILL = "prefill_mfma_kernel<false, 0, 0>" # plain prefill (fp32 log-decay gate)
+GATE = "prefill_mfma_kernel<false, 2, 0>"    # fused gate prologue, bf16 logits
 DECODE = "decode_kernel"
 COPY = "copyBuffer"
 
@@ -102,11 +104,11 @@ def main(dt, df, dw, out):
              "the fused gate prologue) and decode (B=256 H=56 d=128)", "",
              "Commands (from the repository root):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d DIR_T -o trace -- "
-             "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline",
+             "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --segments 0",
              "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR_F -o fetch -- "
-             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration",
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --copy-calibration",
              "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR_W -o write -- "
-             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration",
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --copy-calibration",
              "    python3 bench_traffic.py DIR_T DIR_F DIR_W profiles", "",
              "Kernel source hash: prefill %s, decode %s" % (res["kernel_src_sha"], res["decode_src_sha"]), "",
              "## Kernel trace (--stats)", "", "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
@@ -131,7 +133,44 @@ def main(dt, df, dw, out):
     print(json.dumps({k: res[k] for k in ("fetch_scale", "write_scale", "hbm_bytes_per_launch")}))
 
 
+SEG_KERNELS = (("prefill_mfma_kernel<false, 0, 1>", "pass 1: zero start, no o (segment writes B_p)"),
+               ("prefill_mfma_kernel<false, 0, 2>", "pass 1: identity start, zero values (transition M_p)"),
+               ("fill_identity_kernel", "identity states"),
+               ("combine_kernel", "scan over the segments (incoming states, hT)"),
+               ("prefill_mfma_kernel<false, 0, 0>", "pass 2: from the incoming states, writes o"))
+
+
+def segmented(dt, out, n_seg):
+    """Kernel-trace summary of ``bench.py --segmented-only`` (the segmented prefill alone)."""
+    stats = _csv(dt, "kernel_stats.csv")
+    cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d DIR_T -o trace -- "
+           "python3 bench.py --segmented-only --segments %d --steps 5" % n_seg)
+    lines = ["# rocprofv3: segmented KDA prefill (B=1 H=7 T=262144 d=128, %d segments)" % n_seg, "",
+             "Commands (from the repository root):", "", "    " + cmd,
+             "    python3 bench_traffic.py --segmented %d DIR_T profiles" % n_seg, "",
+             "Kernel source hash: prefill %s, segment combine %s" % (
+                 bench.source_hash(), bench.source_hash([os.path.join(bench._CSRC, "kda_kcp.hip")])), "",
+             "| kernel | role | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    total = 0.0
+    for key, role in SEG_KERNELS:
+        for r in stats:
+            if key in r["Name"]:
+                avg = float(r["AverageNs"]) / 1e3
+                total += avg
+                lines.append("| %s | %s | %d | %.1f | %.1f | %.1f |" % (key, role, int(r["Calls"]), avg,
+                                                                       float(r["MinNs"]) / 1e3,
+                                                                       float(r["MaxNs"]) / 1e3))
+    lines += ["", "Sum of the per-launch averages (one segmented prefill): %.1f us" % total]
+    os.makedirs(out, exist_ok=True)
+    with open(os.path.join(out, "kda_prefill_256k_h7_segmented_rocprof.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
+    if len(sys.argv) == 5 and sys.argv[1] == "--segmented":
+        segmented(sys.argv[3], sys.argv[4], int(sys.argv[2]))
+        sys.exit(0)
     if len(sys.argv) != 5:
         raise SystemExit(__doc__)
     main(*sys.argv[1:])

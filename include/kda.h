@@ -140,6 +140,50 @@ kda_status kda_chunk_fwd_gate(const void *q, const void *k, const void *v,
                               kda_dtype in_dtype, float scale, void *stream);
 
 /*
+ * kda_chunk_fwd_kcp -- kda_chunk_fwd computed as n_seg segments in parallel:
+ * the state-transition split of KDA context parallelism (KCP) in the Kimi K3
+ * paper digest (devpress.csdn.net), section 2.4 (1), on one device.  Over a
+ * segment p the recurrence is affine in its incoming state,
+ *
+ *   S_out = M_p S_in + B_p,
+ *
+ * with B_p the segment's final state from a zero state and M_p its final
+ * state from the identity with zero values (the transition matrix, Dk x Dk).
+ * All segments run side by side from a zero state and from the identity, a
+ * scan over the P maps gives every segment's incoming state (and hT), and all
+ * segments run again from those states to write o.  This fills the device
+ * when B * H alone gives too few work-groups (one long sequence), at the cost
+ * of about three passes over the inputs instead of one.
+ *
+ *   n_seg     number of segments, >= 1; T must be a multiple of n_seg, else
+ *             KDA_ERR_INVALID_ARGUMENT.  n_seg == 1 (or T == 0) is exactly
+ *             kda_chunk_fwd, and ws is then not used.  A segment length that
+ *             is a multiple of 16 keeps the chunks of the single pass.
+ *   ws        device workspace of at least kda_chunk_fwd_kcp_ws_bytes(...)
+ *             bytes, 16-byte aligned, owned by the caller, overwritten, and
+ *             not overlapping any other argument.  Needs Dk == Dv.
+ *   ws_bytes  its size in bytes.
+ *
+ * All other arguments, the layouts and the errors are those of kda_chunk_fwd
+ * (hT == h0 stays allowed).  The results equal kda_chunk_fwd's up to the
+ * rounding of the different summation order.
+ */
+kda_status kda_chunk_fwd_kcp(const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, const float *h0,
+                             float *o, float *hT, int64_t n_seg,
+                             void *ws, uint64_t ws_bytes,
+                             int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                             kda_dtype in_dtype, float scale, void *stream);
+
+/*
+ * kda_chunk_fwd_kcp_ws_bytes -- bytes of workspace kda_chunk_fwd_kcp needs:
+ * three fp32 state sets of [B * n_seg, H, Dk, Dv] (the transitions, the
+ * zero-start states and the incoming states).  0 when n_seg <= 1 or the sizes
+ * are invalid (non-positive, T not a multiple of n_seg, or 64-bit overflow).
+ */
+uint64_t kda_chunk_fwd_kcp_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t n_seg);
+
+/*
  * kda_decode_step -- one new token per sequence (recurrent decoding, the case
  * behind the 4x decoding speed-up at 1M tokens quoted in "Kimi K3
  * Architecture Explained", section 3): the recurrence above with T = 1,

@@ -66,7 +66,11 @@ PREFILL_64K = PrefillConfig("kda_prefill_bf16_b1_h56_t65536_d128", 1, 56, 65536,
 DECODE_B256 = DecodeConfig("kda_decode_bf16_b256_h56_d128", 256, 56, 128, "bf16", 20261204)
 PREFILL_1M = PrefillConfig("kda_prefill_bf16_b1_h56_t1048576_d128_h0", 1, 56, 1 << 20, 128, "bf16", True, 20261205)
 
-PREFILL_CONFIGS = {c.name: c for c in (TINY, PREFILL_B4, PREFILL_64K, PREFILL_1M)}
+# One long sequence on a 7-head share of the 56 heads (the 56 heads split over
+# 8 devices): too few (b, h) pairs to fill the device, the case of the
+# segmented prefill.
+PREFILL_256K_H7 = PrefillConfig("kda_prefill_bf16_b1_h7_t262144_d128", 1, 7, 1 << 18, 128, "bf16", False, 20261206)
+PREFILL_CONFIGS = {c.name: c for c in (TINY, PREFILL_B4, PREFILL_64K, PREFILL_1M, PREFILL_256K_H7)}
 
 
 def torch_dtype(name: str) -> torch.dtype:

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_prefill_valu.hip", "kda_prefill_mfma.hip", "kda_decode.hip"]
+SOURCES = ["kda_api.cpp", "kda_prefill_valu.hip", "kda_prefill_mfma.hip", "kda_decode.hip", "kda_kcp.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -129,11 +129,17 @@ int kda_version(void) { return 100; }  // 0.1.0
 
 namespace {
 
-// The prefill entry points: kda_chunk_fwd is this with no checkpoints.
+kda_status launch_prefill(const kda::PrefillArgs &a, hipStream_t s) {
+    if (kda::prefill_mfma_supported(a)) return launch_status(kda::launch_prefill_mfma(a, s), "kda prefill (mfma)");
+    return launch_status(kda::launch_prefill_valu(a, s), "kda prefill (valu)");
+}
+
+// The prefill entry points: kda_chunk_fwd is this with no checkpoints.  With
+// `out`, the validated arguments are returned instead of launched.
 kda_status chunk_fwd(const void *q, const void *k, const void *v, const void *g, kda::GateMode gate, float g_min,
                      const float *beta, const float *h0, float *o, float *hT, float *ckpt, int64_t ckpt_every,
                      int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale,
-                     void *stream) {
+                     void *stream, kda::PrefillArgs *out = nullptr) {
     if (B <= 0 || H <= 0 || Dk <= 0 || Dv <= 0 || T < 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "sizes must be positive (T >= 0): B=%lld T=%lld H=%lld Dk=%lld Dv=%lld",
                     (long long)B, (long long)T, (long long)H, (long long)Dk, (long long)Dv);
@@ -197,10 +203,12 @@ kda_status chunk_fwd(const void *q, const void *k, const void *v, const void *g,
     a.B = B; a.T = T; a.H = H; a.D = static_cast<int>(Dk);
     a.bf16 = in_dtype == KDA_BF16;
     a.scale = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(Dk));
+    if (out) {
+        *out = a;
+        return ok();
+    }
     if (T == 0 && !hT) return ok();  // nothing to compute or write
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (kda::prefill_mfma_supported(a)) return launch_status(kda::launch_prefill_mfma(a, s), "kda prefill (mfma)");
-    return launch_status(kda::launch_prefill_valu(a, s), "kda prefill (valu)");
+    return launch_prefill(a, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -233,6 +241,88 @@ kda_status kda_chunk_fwd_gate(const void *q, const void *k, const void *v, const
     const kda::GateMode gate = gate_dtype == KDA_BF16 ? kda::kGateLogitBf16 : kda::kGateLogitF32;
     return chunk_fwd(q, k, v, x, gate, g_min, beta, h0, o, hT, nullptr, 0, B, T, H, Dk, Dv, in_dtype, scale,
                      stream);
+}
+
+uint64_t kda_chunk_fwd_kcp_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t n_seg) {
+    if (B <= 0 || T <= 0 || H <= 0 || Dk <= 0 || Dv <= 0 || n_seg <= 1 || T % n_seg != 0) return 0;
+    uint64_t n = 3;
+    if (!mul_ok(n, B) || !mul_ok(n, n_seg) || !mul_ok(n, H) || !mul_ok(n, Dk) || !mul_ok(n, Dv) || n > UINT64_MAX / 4)
+        return 0;
+    return n * 4;
+}
+
+kda_status kda_chunk_fwd_kcp(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                             const float *h0, float *o, float *hT, int64_t n_seg, void *ws, uint64_t ws_bytes,
+                             int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale,
+                             void *stream) {
+    if (n_seg < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "n_seg=%lld must be >= 1", (long long)n_seg);
+    const bool split = n_seg > 1 && T > 0;
+    uint64_t need = 0;
+    if (split && B > 0 && H > 0 && Dk > 0 && Dv > 0) {  // (bad sizes are reported by the prefill checks)
+        if (T % n_seg != 0)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "T=%lld is not a multiple of n_seg=%lld", (long long)T,
+                        (long long)n_seg);
+        need = kda_chunk_fwd_kcp_ws_bytes(B, T, H, Dk, Dv, n_seg);
+        if (need == 0) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace size overflows 64 bits");
+        if (!ws || ws_bytes < need)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "ws (%llu bytes) must hold %llu bytes",
+                        (unsigned long long)ws_bytes, (unsigned long long)need);
+        if (!aligned16(ws)) return fail(KDA_ERR_INVALID_ARGUMENT, "ws is not 16-byte aligned");
+    }
+    kda::PrefillArgs a;
+    kda_status st = chunk_fwd(q, k, v, g, kda::kGateLogDecay, 0.f, beta, h0, o, hT, nullptr, 0, B, T, H, Dk, Dv,
+                              in_dtype, scale, stream, &a);
+    if (st != KDA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!split) {
+        if (T == 0 && !hT) return ok();
+        return launch_prefill(a, s);
+    }
+    const uint64_t esz = in_dtype == KDA_BF16 ? 2 : 4;
+    const uint64_t n_tok = static_cast<uint64_t>(B) * T * H, n_state = static_cast<uint64_t>(B) * H * Dk * Dv;
+    const Span wsp{"ws", ws, need};
+    const Span others[] = {{"q", q, n_tok * Dk * esz}, {"k", k, n_tok * Dk * esz}, {"v", v, n_tok * Dv * esz},
+                           {"g", g, n_tok * Dk * 4},   {"beta", beta, n_tok * 4},  {"h0", h0, n_state * 4},
+                           {"o", o, n_tok * Dv * 4},   {"hT", hT, n_state * 4}};
+    for (const Span &x : others) {
+        if (overlaps(wsp, x)) return fail(KDA_ERR_INVALID_ARGUMENT, "ws overlaps %s", x.name);
+    }
+    st = check_spans(&wsp, 1);
+    if (st != KDA_OK) return st;
+
+    // segments as batch entries: [B, T, ...] is [B * n_seg, T / n_seg, ...]
+    const int64_t L = T / n_seg, BP = B * n_seg;
+    if (BP * H * 64 > INT32_MAX) return fail(KDA_ERR_UNSUPPORTED, "B*n_seg*H too large for one launch");
+    const uint64_t per = static_cast<uint64_t>(BP) * H * Dk * Dv;  // floats of one set of segment states
+    float *M = static_cast<float *>(ws), *Bs = M + per, *S_in = Bs + per;
+    kda::PrefillArgs seg = a;
+    seg.B = BP;
+    seg.T = L;
+    // pass 1: each segment from a zero state (its B_p), and from the identity
+    // with zero values (its M_p); the outputs of these passes are not kept
+    seg.h0 = nullptr;
+    seg.hT = Bs;
+    seg.o = nullptr;
+    st = launch_prefill(seg, s);
+    if (st != KDA_OK) return st;
+    st = launch_status(kda::launch_fill_identity(S_in, BP * H, static_cast<int>(Dk), s), "kda identity fill");
+    if (st != KDA_OK) return st;
+    kda::PrefillArgs tr = seg;
+    tr.v = nullptr;
+    tr.h0 = S_in;
+    tr.hT = M;
+    st = launch_prefill(tr, s);
+    if (st != KDA_OK) return st;
+    // the incoming state of every segment, and the final state
+    st = launch_status(kda::launch_kcp_combine(M, Bs, h0, S_in, hT, B, n_seg, H, static_cast<int>(Dk), s),
+                       "kda segment combine");
+    if (st != KDA_OK) return st;
+    // pass 2: every segment from its incoming state, writing o
+    kda::PrefillArgs fin = seg;
+    fin.h0 = S_in;
+    fin.hT = nullptr;
+    fin.o = o;
+    return launch_prefill(fin, s);
 }
 
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,

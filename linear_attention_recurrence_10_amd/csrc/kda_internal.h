@@ -47,6 +47,10 @@ hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s);
 bool prefill_mfma_supported(const PrefillArgs &a);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+// Segmented prefill helpers (kda_kcp.hip).
+hipError_t launch_fill_identity(float *states, int64_t n, int D, hipStream_t s);
+hipError_t launch_kcp_combine(const float *M, const float *Bs, const float *h0, float *S_in, float *hT, int64_t B,
+                              int64_t P, int64_t H, int D, hipStream_t s);
 
 // g = g_min * sigmoid(x) = g_min / (1 + e^-x): the bounded scaled-sigmoid
 // gate of the Kimi K3 paper digest (devpress.csdn.net), section 2.1 (1), with

@@ -261,8 +261,15 @@ __device__ __forceinline__ void load_kraw(KRaw &r, const PrefillArgs &a, int64_t
     r.beta = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(a.beta + row0) + 4u * off.beta);
 }
 
+// What a launch reads and writes: the full prefill, or one of the passes of
+// the segmented prefill that keep only the final state (kNoOut: no o; kNoValue:
+// no o and zero values, the pass that forms the transition from the identity).
+// Separate instantiations, so that the full prefill carries no test for them.
+enum PassMode { kFull = 0, kNoOut = 1, kNoValue = 2 };
+
 // Values of one chunk for a state lane: token 4g + i, value column `col`;
 // `full` holds the element offsets of a full chunk.
+template <int MODE>
 __device__ __forceinline__ void load_v(uint16_t (&v)[4], const PrefillArgs &a, int64_t t0, int64_t b, int64_t h,
                                        int col, int grp, const uint32_t (&full)[4]) {
     const int64_t T = a.T, H = a.H;
@@ -274,6 +281,11 @@ __device__ __forceinline__ void load_v(uint16_t (&v)[4], const PrefillArgs &a, i
         const int last = static_cast<int>(T - t0) - 1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) off[i] = static_cast<uint32_t>(min(4 * grp + i, last) * HD + col);
+    }
+    if constexpr (MODE == kNoValue) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = 0;
+        return;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const uint16_t *>(vb + 2u * off[i]);
@@ -478,6 +490,7 @@ __device__ __forceinline__ float quad_bcast(float x) {
 // the state update S = diag(e^gamma_C) (S0 + Kh^T U) of this wave's rows.
 // `op` is chunk n's ring slot (M, P are read from it here; the rest is in
 // `cur`), `nx` chunk n + 1's, whose operands are read into `nxt`.
+template <int MODE>
 __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, const Ops &op, const Ops &nx, int64_t n,
                                             int64_t t0, const uint16_t (&vr)[4], f32x4 (&S)[4], const SOps &cur,
                                             SOps &nxt, int64_t b, int64_t h, int rh, int ct, int grp, int n16,
@@ -524,7 +537,7 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
     for (int i = 0; i < 4; ++i) vv[i] = bf16_bits(vr[i]);
     const Sp4 U = split4(mm16(Mf, split4(vv - X), zero));
 
-    if (rh == 0) {
+    if (rh == 0 && MODE == kFull) {
         const f32x4 O = mm16(Pf, U, Y + Yo);
         // o has the layout of v: token 4g + i, column `col` at element offset voff[i]
         char *ob = reinterpret_cast<char *>(a.o + ((b * a.T + t0) * a.H + h) * kD);  // wave uniform
@@ -622,8 +635,8 @@ __device__ __forceinline__ void run_steps(int64_t nchunks, Body &&body) {
 }
 
 // CKPT: the launch writes state checkpoints (a separate instantiation, so the
-// plain prefill carries no test for it).
-template <bool CKPT, int G>  // G: GateMode
+// plain prefill carries no test for it).  MODE: a PassMode.
+template <bool CKPT, int G, int MODE>  // G: GateMode
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     __shared__ Smem sm;
 
@@ -679,8 +692,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             }
         }
         if (nchunks > 0) {
-            load_v(vraw[0], a, 0, b, h, col, grp, voff);
-            load_v(vraw[1], a, nchunks > 1 ? kC : 0, b, h, col, grp, voff);
+            load_v<MODE>(vraw[0], a, 0, b, h, col, grp, voff);
+            load_v<MODE>(vraw[1], a, nchunks > 1 ? kC : 0, b, h, col, grp, voff);
         }
     }
 
@@ -724,9 +737,9 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             constexpr int PAR = decltype(par_tag)::value;
             const int nslot = (sslot == kRing - 1) ? 0 : sslot + 1;  // chunk n + 1
             if constexpr (decltype(state_tag)::value) {
-                state_chunk(a, sm, sm.ops[sslot], sm.ops[nslot], n, n * kC, vraw[PAR], S, so[PAR], so[PAR ^ 1], b, h,
+                state_chunk<MODE>(a, sm, sm.ops[sslot], sm.ops[nslot], n, n * kC, vraw[PAR], S, so[PAR], so[PAR ^ 1], b, h,
                             rh, ct, grp, n16, lane, voff);
-                load_v(vraw[PAR], a, min((n + 2) * kC, last_t0), b, h, col, grp, voff);
+                load_v<MODE>(vraw[PAR], a, min((n + 2) * kC, last_t0), b, h, col, grp, voff);
                 if (CKPT && --ck_left == 0) {  // the state after (ck_i + 1) * ckpt_every chunks
                     if (ck_i < a.n_ckpt) {
                         float *ck = a.ckpt + ck_i * (BH * kD * kD) + sbase;
@@ -773,17 +786,24 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
     const int64_t BH = a.B * a.H;
     const int64_t rounds = (BH + 7) / 8;
     const dim3 grid(static_cast<unsigned>(rounds * 8 * kNV));
-    // checkpoints are written with the fp32 log-decay gate only (the entry
-    // points offer no other combination)
+    // checkpoints, and the passes without o, come with the fp32 log-decay gate
+    // only (the entry points offer no other combination)
+    const bool plain = !a.ckpt && a.gate == kGateLogDecay;
+    if ((!a.o || !a.v) && !plain) return hipErrorInvalidValue;
+    if (!a.v && a.o) return hipErrorInvalidValue;
     if (a.ckpt && a.gate != kGateLogDecay) return hipErrorInvalidValue;
     if (a.ckpt)
-        hipLaunchKernelGGL((prefill_mfma_kernel<true, kGateLogDecay>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((prefill_mfma_kernel<true, kGateLogDecay, kFull>), grid, dim3(kThreads), 0, s, a);
     else if (a.gate == kGateLogitF32)
-        hipLaunchKernelGGL((prefill_mfma_kernel<false, kGateLogitF32>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((prefill_mfma_kernel<false, kGateLogitF32, kFull>), grid, dim3(kThreads), 0, s, a);
     else if (a.gate == kGateLogitBf16)
-        hipLaunchKernelGGL((prefill_mfma_kernel<false, kGateLogitBf16>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((prefill_mfma_kernel<false, kGateLogitBf16, kFull>), grid, dim3(kThreads), 0, s, a);
+    else if (!a.v)
+        hipLaunchKernelGGL((prefill_mfma_kernel<false, kGateLogDecay, kNoValue>), grid, dim3(kThreads), 0, s, a);
+    else if (!a.o)
+        hipLaunchKernelGGL((prefill_mfma_kernel<false, kGateLogDecay, kNoOut>), grid, dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((prefill_mfma_kernel<false, kGateLogDecay>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((prefill_mfma_kernel<false, kGateLogDecay, kFull>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(DVS *RG) void prefill_valu_kernel(PrefillArgs a) {
         for (int e = tid; e < C * DVS; e += NT) {
             const int r = e / DVS, j = e % DVS;
             const int64_t t = t0 + r;
-            sV[r][j] = (t < T) ? ld_elem(v, ((b * T + t) * H + h) * D + nv * DVS + j) : 0.f;
+            sV[r][j] = (t < T && v) ? ld_elem(v, ((b * T + t) * H + h) * D + nv * DVS + j) : 0.f;
         }
         if (tid < C) {
             const int64_t t = t0 + tid;
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(DVS *RG) void prefill_valu_kernel(PrefillArgs a) {
         // (6) O = scale * (Qb S0 + P U); lane rg stores rows r = rg (mod RG)
 #pragma unroll
         for (int r = 0; r < C; ++r) {
-            if ((r % RG) == rg && t0 + r < T) {
+            if ((r % RG) == rg && t0 + r < T && a.o) {
                 float acc = qs[r];
 #pragma unroll
                 for (int s = 0; s <= r; ++s) acc += sP[r][s] * u[s];

@@ -176,3 +176,42 @@ def test_gate_shares_the_prefill_checks(lib):
     ptrs[6] = ctypes.c_void_p(ptrs[3].value + 64)   # o inside the logits
     assert chunk_gate(lib, ptrs=ptrs) == 1
     assert b"o overlaps g" in lib.kda_last_error()
+
+
+# ---- the segmented prefill (kda_chunk_fwd_kcp) ----
+
+def chunk_kcp(lib, n_seg=4, T=64, ws=0x7000000, ws_bytes=1 << 30, B=1, H=1, D=128):
+    p = [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(8)]
+    return lib.kda_chunk_fwd_kcp(*p, n_seg, ctypes.c_void_p(ws) if ws else None, ws_bytes, B, T, H, D, D, 1,
+                                 0.0, None)
+
+
+def test_kcp_workspace_size(lib):
+    assert kda.kcp_ws_bytes(2, 64, 3, 128, 128, 4) == 3 * 2 * 4 * 3 * 128 * 128 * 4
+    assert kda.kcp_ws_bytes(1, 64, 1, 16, 16, 1) == 0      # one segment: no workspace
+    assert kda.kcp_ws_bytes(1, 65, 1, 16, 16, 4) == 0      # not a multiple
+    assert kda.kcp_ws_bytes(0, 64, 1, 16, 16, 4) == 0
+    assert kda.kcp_ws_bytes(1 << 40, 1 << 20, 1 << 20, 128, 128, 2) == 0   # overflow
+
+
+@pytest.mark.parametrize("n_seg", [0, -2])
+def test_kcp_segment_count_positive(lib, n_seg):
+    assert chunk_kcp(lib, n_seg=n_seg) == 1
+    assert b"n_seg" in lib.kda_last_error()
+
+
+def test_kcp_length_must_divide(lib):
+    assert chunk_kcp(lib, n_seg=3, T=64) == 1
+    assert b"multiple of n_seg" in lib.kda_last_error()
+
+
+def test_kcp_workspace_checks(lib):
+    need = kda.kcp_ws_bytes(1, 64, 1, 128, 128, 4)
+    assert chunk_kcp(lib, ws=0) == 1 and b"ws" in lib.kda_last_error()
+    assert chunk_kcp(lib, ws_bytes=need - 4) == 1 and b"must hold" in lib.kda_last_error()
+    assert chunk_kcp(lib, ws=0x7000008) == 1 and b"aligned" in lib.kda_last_error()
+
+
+def test_kcp_shares_the_prefill_checks(lib):
+    assert chunk_kcp(lib, n_seg=1, D=64) == 2          # one segment is the plain prefill
+    assert chunk_kcp(lib, B=0) == 1 and b"sizes" in lib.kda_last_error()

@@ -1,0 +1,137 @@
+"""The segmented prefill (kda_chunk_fwd_kcp) against the fp64 oracle.
+
+o and hT must match the whole-sequence oracle for every segment count (the
+split is exact up to rounding); the workspace's transition matrices,
+zero-start states and incoming states must match the segment-parallel
+oracle's (``oracle.kcp``), which builds the transitions from explicit
+per-token matrices; and one segment must be exactly kda_chunk_fwd.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+import linear_attention_recurrence_10_amd as kda
+from gpu_helpers import host64, oracle_full, rel_err, tol_for
+from oracle.kcp import kcp_fwd
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+# A slow-decay gate (mean log-decay about -0.012 per channel and token): the
+# state carried across a segment boundary then still counts in o and hT.
+SLOW = -6.0
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_kcp(x, n_seg, h0=None, hT=None, ws=None, output_final_state=True):
+    return kda.chunk_fwd_kcp(x["q"], x["k"], x["v"], x["g"], x["beta"], h0, n_seg=n_seg, ws=ws, hT=hT,
+                             output_final_state=output_final_state)
+
+
+@pytest.mark.parametrize("gate_mean", [SLOW, 0.0])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 128), ("f32", 16)])
+@pytest.mark.parametrize("T,n_seg", [(256, 2), (256, 4), (259, 7), (96, 6), (64, 64)])
+def test_kcp_matches_oracle(dtype, D, T, n_seg, gate_mean):
+    say("case kcp dtype=%s D=%d T=%d n_seg=%d gate_mean=%g" % (dtype, D, T, n_seg, gate_mean))
+    x = kda_inputs.prefill_inputs(2, T, 3, D, dtype, h0=True, seed=71, device=DEV, gate_mean=gate_mean)
+    o, hT = run_kcp(x, n_seg, x["h0"])
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle_full(x)
+    eo, eh = rel_err(o.cpu(), o_ref), rel_err(hT.cpu(), h_ref)
+    say("  o err=%.3e hT err=%.3e" % (eo, eh))
+    tol = tol_for(dtype)
+    assert eo <= tol and eh <= tol
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 16)])
+def test_kcp_workspace_holds_the_segment_maps(dtype, D):
+    """The workspace is [M, Bs, S_in], each [B * n_seg, H, D, D] fp32."""
+    B, T, H, P = 2, 192, 3, 3
+    say("case kcp workspace dtype=%s D=%d" % (dtype, D))
+    x = kda_inputs.prefill_inputs(B, T, H, D, dtype, h0=True, seed=72, device=DEV, gate_mean=SLOW)
+    ws = torch.empty(kda.kcp_ws_bytes(B, T, H, D, D, P), dtype=torch.uint8, device=DEV)
+    run_kcp(x, P, x["h0"], ws=ws)
+    torch.cuda.synchronize()
+    parts = ws.view(torch.float32).view(3, B, P, H, D, D).cpu()
+    args = [host64(x[n]) for n in ("q", "k", "v", "g", "beta")]
+    _, _, ref = kcp_fwd(*args, h0=host64(x["h0"]), n_seg=P)
+    tol = tol_for(dtype)
+    for i, name in enumerate(("M", "Bs", "S_in")):
+        e = rel_err(parts[i], ref[name])
+        say("  %s err=%.3e" % (name, e))
+        assert e <= tol, name
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 16)])
+def test_kcp_one_segment_is_the_plain_prefill(dtype, D):
+    x = kda_inputs.prefill_inputs(1, 100, 2, D, dtype, h0=True, seed=73, device=DEV)
+    o1, h1 = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+    o2, h2 = run_kcp(x, 1, x["h0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def test_kcp_segments_agree_with_the_plain_prefill():
+    """Several segments against the single pass: equal up to the summation order."""
+    x = kda_inputs.prefill_inputs(1, 2048, 4, 128, "bf16", h0=True, seed=74, device=DEV, gate_mean=SLOW)
+    o1, h1 = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+    for P in (2, 8, 16):
+        o2, h2 = run_kcp(x, P, x["h0"])
+        torch.cuda.synchronize()
+        eo, eh = rel_err(o2.cpu(), host64(o1)), rel_err(h2.cpu(), host64(h1))
+        say("  P=%d vs single pass: o %.3e hT %.3e" % (P, eo, eh))
+        assert eo <= 1e-2 and eh <= 1e-2
+
+
+def test_kcp_state_in_place_and_no_final_state():
+    x = kda_inputs.prefill_inputs(2, 128, 2, 128, "bf16", h0=True, seed=75, device=DEV, gate_mean=SLOW)
+    o_ref, h_ref = oracle_full(x)
+    state = x["h0"].clone()
+    o, hT = run_kcp(x, 4, state, hT=state)           # hT aliases h0
+    o2, none = run_kcp(x, 4, x["h0"], output_final_state=False)
+    torch.cuda.synchronize()
+    assert hT.data_ptr() == state.data_ptr() and none is None
+    assert rel_err(state.cpu(), h_ref) <= tol_for("bf16")
+    assert rel_err(o.cpu(), o_ref) <= tol_for("bf16") and torch.equal(o, o2)
+
+
+def test_kcp_zero_initial_state_and_reused_workspace():
+    """Without h0, and a workspace reused by a second, smaller call."""
+    ws = torch.empty(kda.kcp_ws_bytes(2, 256, 3, 128, 128, 4), dtype=torch.uint8, device=DEV)
+    for T, P in ((256, 4), (96, 2)):
+        x = kda_inputs.prefill_inputs(2, T, 3, 128, "bf16", h0=False, seed=76 + T, device=DEV, gate_mean=SLOW)
+        o, hT = run_kcp(x, P, None, ws=ws)
+        torch.cuda.synchronize()
+        o_ref, h_ref = oracle_full(x)
+        assert rel_err(o.cpu(), o_ref) <= tol_for("bf16") and rel_err(hT.cpu(), h_ref) <= tol_for("bf16")
+
+
+def test_kcp_rejects_overlapping_workspace():
+    x = kda_inputs.prefill_inputs(1, 64, 2, 16, "f32", h0=False, seed=77, device=DEV)
+    need = kda.kcp_ws_bytes(1, 64, 2, 16, 16, 4)
+    buf = torch.empty(need, dtype=torch.uint8, device=DEV)
+    o = buf[:64 * 2 * 16 * 4].view(torch.float32).view(1, 64, 2, 16)   # o inside the workspace
+    with pytest.raises(kda.KdaError, match="ws overlaps o"):
+        kda.chunk_fwd_kcp(x["q"], x["k"], x["v"], x["g"], x["beta"], n_seg=4, o=o, ws=buf)
+
+
+def test_kcp_long_sequence_sampled():
+    """One long sequence in 16 segments: sampled heads and columns against the oracle."""
+    from gpu_helpers import oracle_sampled, pick
+    x = kda_inputs.prefill_inputs(1, 8192, 8, 128, "bf16", h0=True, seed=78, device=DEV, gate_mean=SLOW)
+    o, hT = run_kcp(x, 16, x["h0"])
+    torch.cuda.synchronize()
+    heads, cols = [0, 5], [0, 37, 127]
+    o_ref, s_ref = oracle_sampled(x, heads, cols)
+    eo = rel_err(pick(o, heads, cols), o_ref)
+    eh = rel_err(pick(hT, heads, cols, head_dim=1, col_dim=3), s_ref)
+    say("  T=8192 P=16: o %.3e hT %.3e" % (eo, eh))
+    assert eo <= tol_for("bf16") and eh <= tol_for("bf16")
