@@ -79,6 +79,7 @@ using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
 using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 using f32x2 = float __attribute__((ext_vector_type(2)));
 using bf16x2 = __bf16 __attribute__((ext_vector_type(2)));
+using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;     // head dimension (d_k = d_v)
 constexpr int kDVS = 32;    // value columns per work-group
@@ -203,6 +204,7 @@ struct Ops {
     f32x4 eq[2][4][4];       // e^gamma_C: [rh][g][q] holds channels 64 rh + 16 t + 4 g + q, t = 0..3
     bf16x4 Mhl[2][64];       // M = (I + A)^-1 diag(beta), split [hi, lo][lane], A-operand layout
     bf16x4 P[2][64];         // P split [hi, lo][lane]: lane (n, g) holds row n, columns 4g .. 4g + 3
+    uint16_t vt[kDVS][kC];   // v of the work-group's columns, transposed: [column][token]
 };
 
 struct Smem {
@@ -212,6 +214,51 @@ struct Smem {
     f32x4 arow[4][kC][5];         // summed, masked A per solver wave; rows padded to 80 bytes
     f32x4 xy[2][2][2][64];        // partial X, Y [row half][X, Y][column tile][lane]
     uint32_t flag[2][2];          // state-wave handshake [column tile][row half]
+};
+
+// Global loads and stores go through buffer descriptors: the chunk's base
+// address and the number of bytes up to its last token are wave-uniform
+// (scalar registers), and each lane adds its fixed 32-bit byte offset.  In a
+// last, partial chunk the offsets of tokens past the end lie beyond the
+// descriptor's range, so the hardware returns zeros for those loads and drops
+// those stores: no per-lane clamp or test.  Offsets stay below 2^31 bytes for
+// the head counts this kernel accepts.
+using Rsrc = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                            kRsrcWord3);
+}
+
+// Chunk c of one (b, h) sequence: its tokens are c kC .. c kC + rem - 1, with
+// rem = kC except in the last chunk.  A [B, T, H, W] tensor's chunk starts
+// c kC H W elements after the sequence's base, and its bytes up to the end of
+// the last token's W elements are span_rows(c) W esz, where span_rows counts
+// the rows of W elements from the chunk start: (rem - 1) H + 1.  All values
+// are wave uniform and 32-bit.
+struct Geom {
+    int H;      // heads
+    int nlast;  // index of the last chunk
+    int tail;   // tokens of the last chunk, 1 .. kC
+};
+__device__ __forceinline__ uint32_t span_rows(const Geom &g, int c) {
+    const int rem = c < g.nlast ? kC : g.tail;
+    return static_cast<uint32_t>((rem - 1) * g.H + 1);
+}
+// The descriptor of chunk c of a tensor with W elements of esz bytes per
+// (token, head), from the sequence's base address.
+template <int W, int ESZ>
+__device__ __forceinline__ Rsrc chunk_rsrc(const void *seq_base, const Geom &g, int c) {
+    const char *p = static_cast<const char *>(seq_base) +
+                    static_cast<uint64_t>(static_cast<uint32_t>(c)) * static_cast<uint32_t>(kC * g.H * W * ESZ);
+    return make_rsrc(p, span_rows(g, c) * (W * ESZ));
+}
+
+// The sequence bases of one (b, h): token 0 of each input and of o.
+struct SeqBase {
+    const void *q, *k, *v, *g, *beta;
+    float *o;
 };
 
 // Raw inputs of one chunk for a k-side lane: q, k (4 bf16 per 16-channel
@@ -224,11 +271,6 @@ struct KRaw {
     float beta;
 };
 
-// Loads never branch per element and never leave the sequence: in a last,
-// partial chunk the token index is clamped.  Offsets are unsigned 32-bit
-// element offsets (16 tokens of a row of H heads stay below 2^31 bytes for
-// the head counts this kernel accepts) added to a wave-uniform 64-bit base;
-// the offsets of full chunks are loop invariants computed once.
 struct KOff {
     uint32_t tok;   // token n, channel 32 kw + 4 g (elements)
     uint32_t beta;  // token n (elements of beta)
@@ -238,27 +280,24 @@ __device__ __forceinline__ KOff kraw_offsets(const PrefillArgs &a, int tok, int 
     return KOff{static_cast<uint32_t>(tok * HD + 32 * kw + 4 * grp), static_cast<uint32_t>(tok * static_cast<int>(a.H))};
 }
 template <int G>  // GateMode
-__device__ __forceinline__ void load_kraw(KRaw &r, const PrefillArgs &a, int64_t t0, int64_t b, int64_t h, int kw,
-                                          int grp, int n16, const KOff &full) {
-    const int64_t T = a.T, H = a.H;
-    const int64_t row0 = (b * T + t0) * H + h;  // token row of the chunk start (wave uniform)
-    KOff off = full;
-    if (t0 + kC > T) off = kraw_offsets(a, min(n16, static_cast<int>(T - t0) - 1), kw, grp);
-    const uint32_t e0 = off.tok;
-    const char *gb = reinterpret_cast<const char *>(a.g) + (G == kGateLogitBf16 ? 2 : 4) * (row0 * kD);
-    const char *qb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.q) + row0 * kD);
-    const char *kb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k) + row0 * kD);
+__device__ __forceinline__ void load_kraw(KRaw &r, const SeqBase &sb, const Geom &gm, int c, const KOff &off) {
+    const Rsrc rq = chunk_rsrc<kD, 2>(sb.q, gm, c);
+    const Rsrc rk = chunk_rsrc<kD, 2>(sb.k, gm, c);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-        const uint32_t e = e0 + 16u * tt;
-        r.q[tt] = *reinterpret_cast<const u32x2 *>(qb + 2u * e);
-        r.k[tt] = *reinterpret_cast<const u32x2 *>(kb + 2u * e);
-        if constexpr (G == kGateLogitBf16)
-            r.gx[tt] = *reinterpret_cast<const u32x2 *>(gb + 2u * e);
-        else
-            r.g[tt] = *reinterpret_cast<const f32x4 *>(gb + 4u * e);
+        const uint32_t e = off.tok + 16u * tt;
+        r.q[tt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rq, 2u * e, 0, 0));
+        r.k[tt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, 2u * e, 0, 0));
+        if constexpr (G == kGateLogitBf16) {
+            const Rsrc rg = chunk_rsrc<kD, 2>(sb.g, gm, c);
+            r.gx[tt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, 2u * e, 0, 0));
+        } else {
+            const Rsrc rg = chunk_rsrc<kD, 4>(sb.g, gm, c);
+            r.g[tt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, 4u * e, 0, 0));
+        }
     }
-    r.beta = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(a.beta + row0) + 4u * off.beta);
+    const Rsrc rb = chunk_rsrc<1, 4>(sb.beta, gm, c);
+    r.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4u * off.beta, 0, 0));
 }
 
 // What a launch reads and writes: the full prefill, or one of the passes of
@@ -267,28 +306,21 @@ __device__ __forceinline__ void load_kraw(KRaw &r, const PrefillArgs &a, int64_t
 // Separate instantiations, so that the full prefill carries no test for them.
 enum PassMode { kFull = 0, kNoOut = 1, kNoValue = 2 };
 
-// Values of one chunk for a state lane: token 4g + i, value column `col`;
-// `full` holds the element offsets of a full chunk.
-template <int MODE>
-__device__ __forceinline__ void load_v(uint16_t (&v)[4], const PrefillArgs &a, int64_t t0, int64_t b, int64_t h,
-                                       int col, int grp, const uint32_t (&full)[4]) {
-    const int64_t T = a.T, H = a.H;
-    const int64_t row0 = (b * T + t0) * H + h;
-    const char *vb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.v) + row0 * kD);
-    const int HD = static_cast<int>(H) * kD;
-    uint32_t off[4] = {full[0], full[1], full[2], full[3]};
-    if (t0 + kC > T) {
-        const int last = static_cast<int>(T - t0) - 1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) off[i] = static_cast<uint32_t>(min(4 * grp + i, last) * HD + col);
-    }
-    if constexpr (MODE == kNoValue) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = 0;
-        return;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const uint16_t *>(vb + 2u * off[i]);
+// Values of one chunk for a state lane: token 4g + i, value column `col`,
+// at byte offset vb0 + i sv (vb0 per lane, the row step sv wave uniform;
+// tokens past the end read as zero).
+// The values of a chunk are staged by the solver waves: solver lane (wave sv,
+// lane l) holds token 4 sv + l / 16, columns 2 (l % 16) and 2 (l % 16) + 1 of
+// the work-group's 32, as one dword at byte offset vb0 (tokens past the end
+// read as zero), and writes them into the chunk's ring slot transposed, where
+// a state lane finds its four tokens 4g .. 4g + 3 of one column in 8 bytes.
+__device__ __forceinline__ uint32_t load_v2(const SeqBase &sb, const Geom &gm, int c, uint32_t vb0) {
+    return __builtin_amdgcn_raw_buffer_load_b32(chunk_rsrc<kD, 2>(sb.v, gm, c), vb0, 0, 0);
+}
+__device__ __forceinline__ void stage_v2(Ops &op, uint32_t v2, int sv, int lane) {
+    const int t = 4 * sv + (lane >> 4), c = 2 * (lane & 15);
+    op.vt[c][t] = static_cast<uint16_t>(v2);
+    op.vt[c + 1][t] = static_cast<uint16_t>(v2 >> 16);
 }
 
 // Unpacked inputs of one chunk for a k-side lane (channel slot j of token n).
@@ -486,15 +518,15 @@ __device__ __forceinline__ float quad_bcast(float x) {
     return dpp_move<I * 0x55>(x);
 }
 
-// State part of chunk n (start t0) for state wave (rh, ct): X, Y, U, O and
+// State part of chunk n for state wave (rh, ct): X, Y, U, O and
 // the state update S = diag(e^gamma_C) (S0 + Kh^T U) of this wave's rows.
 // `op` is chunk n's ring slot (M, P are read from it here; the rest is in
 // `cur`), `nx` chunk n + 1's, whose operands are read into `nxt`.
 template <int MODE>
 __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, const Ops &op, const Ops &nx, int64_t n,
-                                            int64_t t0, const uint16_t (&vr)[4], f32x4 (&S)[4], const SOps &cur,
-                                            SOps &nxt, int64_t b, int64_t h, int rh, int ct, int grp, int n16,
-                                            int lane, const uint32_t (&voff)[4]) {
+                                            const SeqBase &sb, const Geom &gm, f32x4 (&S)[4],
+                                            const SOps &cur, SOps &nxt, int rh, int ct, int grp, int n16, int lane,
+                                            uint32_t ob0, uint32_t so) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const Sp4 Mf = Sp4{op.Mhl[0][lane], op.Mhl[1][lane]};
     const Sp4 Pf = Sp4{op.P[0][lane], op.P[1][lane]};
@@ -532,25 +564,23 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
     read_kq(nxt, nx, rh, lane);
     X += Xo;
 
-    f32x4 vv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vv[i] = bf16_bits(vr[i]);
+    f32x4 vv = zero;
+    if constexpr (MODE != kNoValue) {
+        const u32x2 vp = *reinterpret_cast<const u32x2 *>(&op.vt[16 * ct + (lane & 15)][4 * grp]);
+        vv[0] = __uint_as_float(vp[0] << 16);
+        vv[1] = __uint_as_float(vp[0] & 0xffff0000u);
+        vv[2] = __uint_as_float(vp[1] << 16);
+        vv[3] = __uint_as_float(vp[1] & 0xffff0000u);
+    }
     const Sp4 U = split4(mm16(Mf, split4(vv - X), zero));
 
     if (rh == 0 && MODE == kFull) {
         const f32x4 O = mm16(Pf, U, Y + Yo);
-        // o has the layout of v: token 4g + i, column `col` at element offset voff[i]
-        char *ob = reinterpret_cast<char *>(a.o + ((b * a.T + t0) * a.H + h) * kD);  // wave uniform
-        if (t0 + kC <= a.T) {
+        // o has the layout of v: token 4g + i, column `col` at byte offset ob0 + i so
+        const Rsrc ro = chunk_rsrc<kD, 4>(sb.o, gm, static_cast<int>(n));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) *reinterpret_cast<float *>(ob + 4u * voff[i]) = a.scale * O[i];
-        } else {
-            const int left = static_cast<int>(a.T - t0);  // tokens of the last, partial chunk
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (4 * grp + i < left) *reinterpret_cast<float *>(ob + 4u * voff[i]) = a.scale * O[i];
-            }
-        }
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, a.scale * O[i]), ro, ob0, i * so, 0);
     }
 
     // S: lane (n, g) holds rows 4g + i of tile t, channel 64 rh + 16 t + 4 g + i,
@@ -671,16 +701,27 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     if (tid < 4) (&sm.flag[0][0])[tid] = 0u;
 
     const KOff koff = kraw_offsets(a, n16, kw, grp);
-    uint32_t voff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) voff[i] = static_cast<uint32_t>((4 * grp + i) * static_cast<int>(a.H) * kD + col);
+    // a state lane's token 4 grp + i, column col of o: element offset
+    // voff0 + i HD within a chunk (the row step HD is wave uniform)
+    const uint32_t HD = static_cast<uint32_t>(a.H) * kD;
+    const uint32_t voff0 = static_cast<uint32_t>(4 * grp) * HD + static_cast<uint32_t>(col);
+    // a solver lane's dword of v: token 4 sv + lane / 16, columns col0 + 2 (lane % 16) + {0, 1}
+    const uint32_t vb0 = 2u * (static_cast<uint32_t>(4 * sv + (lane >> 4)) * HD +
+                               static_cast<uint32_t>(col0 + 2 * (lane & 15)));
+    const int64_t seq_row = b * T * a.H + h;  // token 0 of this (b, h), in rows of kD elements
+    const SeqBase sb{static_cast<const uint16_t *>(a.q) + seq_row * kD, static_cast<const uint16_t *>(a.k) + seq_row * kD,
+                     static_cast<const uint16_t *>(a.v) + seq_row * kD,
+                     static_cast<const char *>(a.g) + (G == kGateLogitBf16 ? 2 : 4) * (seq_row * kD),
+                     a.beta + seq_row, a.o ? a.o + seq_row * kD : nullptr};
+    const int nlast = static_cast<int>(nchunks) - 1;
+    const Geom gm{static_cast<int>(a.H), nlast, static_cast<int>(T - static_cast<int64_t>(nlast) * kC)};
     KRaw raw[2];
     f32x4 S[4];  // state rows 64 rh + 16 t + 4 g + i, column `col`
-    uint16_t vraw[2][4];
+
     if (kwave) {
         if (nchunks > 0) {
-            load_kraw<G>(raw[0], a, 0, b, h, kw, grp, n16, koff);
-            load_kraw<G>(raw[1], a, nchunks > 1 ? kC : 0, b, h, kw, grp, n16, koff);
+            load_kraw<G>(raw[0], sb, gm, 0, koff);
+            load_kraw<G>(raw[1], sb, gm, min(1, nlast), koff);
         }
     } else if (swave) {
 #pragma unroll
@@ -691,10 +732,6 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
                 S[t][i] = a.h0 ? a.h0[sbase + row * kD + col] : 0.f;
             }
         }
-        if (nchunks > 0) {
-            load_v<MODE>(vraw[0], a, 0, b, h, col, grp, voff);
-            load_v<MODE>(vraw[1], a, nchunks > 1 ? kC : 0, b, h, col, grp, voff);
-        }
     }
 
     // Step n: the k-side waves prepare chunk n + 2, the solver waves solve
@@ -702,7 +739,6 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     // Each role runs its own copy of the step sequence, so the register
     // double-buffers of one role never meet another's in a loop phi, and
     // loaded values are consumed in the registers they land in.
-    const int64_t last_t0 = nchunks > 0 ? (nchunks - 1) * kC : 0;
     if (kwave) {
         int kslot = 0;  // ring slot of chunk n + 2
         run_steps(nchunks, [&](auto par_tag, auto, auto kside_tag, auto, int64_t n) {
@@ -712,17 +748,24 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             if constexpr (decltype(kside_tag)::value) kside_in<G>(a, raw[PAR], in, (n + 2) * kC, n16);
             if constexpr (decltype(kside_tag)::value) {
                 kside(sm.ops[kslot], sm.gram[PAR], sm.beta[PAR], in, kw, grp, n16, lane);
-                load_kraw<G>(raw[PAR], a, min((n + 4) * kC, last_t0), b, h, kw, grp, n16, koff);
+                load_kraw<G>(raw[PAR], sb, gm, min(static_cast<int>(n) + 4, nlast), koff);
             }
             kslot = (kslot == kRing - 1) ? 0 : kslot + 1;
         });
     } else if (!swave) {
         int vslot = 2;  // ring slot of chunk n + 1 (n = -2 maps to slot 2)
-        run_steps(nchunks, [&](auto par_tag, auto solve_tag, auto, auto, int64_t) {
+        uint32_t v2 = 0;  // this lane's values of chunk n + 1, loaded one step ahead
+        if (MODE != kNoValue && nchunks > 0) v2 = load_v2(sb, gm, 0, vb0);
+        run_steps(nchunks, [&](auto par_tag, auto solve_tag, auto, auto, int64_t n) {
             constexpr int PAR = decltype(par_tag)::value;  // n & 1
-            if constexpr (decltype(solve_tag)::value)
+            if constexpr (decltype(solve_tag)::value) {
+                if constexpr (MODE != kNoValue) {
+                    stage_v2(sm.ops[vslot], v2, sv, lane);
+                    v2 = load_v2(sb, gm, min(static_cast<int>(n) + 2, nlast), vb0);
+                }
                 solve(sm.gram[PAR ^ 1], sm.beta[PAR ^ 1], sm.arow[sv], sm.ops[vslot].Mhl, sm.ops[vslot].P, sv, grp,
                       n16, lane);
+            }
             vslot = (vslot == kRing - 1) ? 0 : vslot + 1;
         });
     } else {
@@ -737,9 +780,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             constexpr int PAR = decltype(par_tag)::value;
             const int nslot = (sslot == kRing - 1) ? 0 : sslot + 1;  // chunk n + 1
             if constexpr (decltype(state_tag)::value) {
-                state_chunk<MODE>(a, sm, sm.ops[sslot], sm.ops[nslot], n, n * kC, vraw[PAR], S, so[PAR], so[PAR ^ 1], b, h,
-                            rh, ct, grp, n16, lane, voff);
-                load_v<MODE>(vraw[PAR], a, min((n + 2) * kC, last_t0), b, h, col, grp, voff);
+                state_chunk<MODE>(a, sm, sm.ops[sslot], sm.ops[nslot], n, sb, gm, S, so[PAR], so[PAR ^ 1], rh, ct,
+                                  grp, n16, lane, 4u * voff0, 4u * HD);
                 if (CKPT && --ck_left == 0) {  // the state after (ck_i + 1) * ckpt_every chunks
                     if (ck_i < a.n_ckpt) {
                         float *ck = a.ckpt + ck_i * (BH * kD * kD) + sbase;
