@@ -203,6 +203,7 @@ kda_status chunk_fwd(const void *q, const void *k, const void *v, const void *g,
     a.B = B; a.T = T; a.H = H; a.D = static_cast<int>(Dk);
     a.bf16 = in_dtype == KDA_BF16;
     a.scale = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(Dk));
+    a.epoch = 0;
     if (out) {
         *out = a;
         return ok();

@@ -28,6 +28,7 @@ struct PrefillArgs {
     int D;
     bool bf16;
     float scale;
+    uint32_t epoch;          // launch tag of the value slices' pacing (set by the MFMA launcher)
 };
 
 struct DecodeArgs {

@@ -63,6 +63,7 @@
 // tiles token-major and the state waves read them with gfx950's transposing
 // LDS read, which delivers that layout.  The Grams are formed transposed (Kh Kb^T, Kh Qb^T), so their result layout is
 // "row n, columns 4g + i", the A-operand layout of U = M Z and P U.
+#include <atomic>
 #include <cstdlib>
 #include <type_traits>
 
@@ -216,13 +217,53 @@ struct Smem {
     uint32_t flag[2][2];          // state-wave handshake [column tile][row half]
 };
 
-// Global loads and stores go through buffer descriptors: the chunk's base
-// address and the number of bytes up to its last token are wave-uniform
-// (scalar registers), and each lane adds its fixed 32-bit byte offset.  In a
-// last, partial chunk the offsets of tokens past the end lie beyond the
-// descriptor's range, so the hardware returns zeros for those loads and drops
-// those stores: no per-lane clamp or test.  Offsets stay below 2^31 bytes for
-// the head counts this kernel accepts.
+// Pacing of the four value slices of one (b, h).  They run on four compute
+// units of one XCD and read the same q, k and g, so the XCD's L2 serves the
+// three later readers of each line only while the slices stay within some
+// twenty steps of each other; left alone they drift apart by tens of steps
+// over a long sequence and then read those lines from HBM again.  Every
+// kPaceEvery steps one solver wave reports its step and reads the others'
+// reports (consumed one step later, so no load latency is waited for).  A
+// report is up to kPaceEvery steps old when read, so a slice polls only when
+// it leads a started slice of its head by more than kPaceEvery + kPaceLead
+// steps by the reports, i.e. by more than kPaceLead steps at least, until it
+// no longer does (at most kPaceSpin polls); the small offsets of slices that
+// keep pace never cause a wait.  Reports carry the launch's epoch,
+// so those of other launches never count, and the slowest slice never waits.
+// The pacing only delays work: no result depends on it.
+constexpr int kPaceSlots = 1 << 16;  // 4 per (b, h): launches with B H <= 16384 are paced
+constexpr int kPaceEvery = 8;
+constexpr int kPaceLead = 6;
+constexpr int kPaceSpin = 4096;
+__device__ uint64_t g_pace[kPaceSlots];
+
+// Reports of the slices of one (b, h): lane s < 4 reads slice s's entry.
+__device__ __forceinline__ uint64_t pace_read(const uint64_t *e, int lane) {
+    return lane < 4 ? __hip_atomic_load(e + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : ~0ull;
+}
+// Steps this slice (at step n, slice nv) leads the slowest other started slice.
+__device__ __forceinline__ int64_t pace_lead(uint64_t rep, uint32_t epoch, int64_t n, int nv, int lane) {
+    const bool mine = lane < 4 && lane != nv && static_cast<uint32_t>(rep >> 32) == epoch;
+    const int64_t step = mine ? static_cast<int64_t>(static_cast<uint32_t>(rep)) : INT64_MAX;
+    int64_t lo = INT64_MAX;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint32_t x_lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(step), s));
+        const uint32_t x_hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(step >> 32), s));
+        const int64_t x = static_cast<int64_t>((static_cast<uint64_t>(x_hi) << 32) | x_lo);
+        lo = x < lo ? x : lo;
+    }
+    return lo == INT64_MAX ? 0 : n - lo;
+}
+
+// The values (loaded by the solver waves) and o (stored by the state waves)
+// go through buffer descriptors: the chunk's base address and the number of
+// bytes up to its last token are wave-uniform (scalar registers), and each
+// lane adds its fixed 32-bit byte offset.  In a last, partial chunk the
+// offsets of tokens past the end lie beyond the descriptor's range, so the
+// hardware returns zeros for those loads and drops those stores: no per-lane
+// clamp or test.  Offsets stay below 2^31 bytes for the head counts this
+// kernel accepts.
 using Rsrc = __amdgpu_buffer_rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
@@ -257,7 +298,8 @@ __device__ __forceinline__ Rsrc chunk_rsrc(const void *seq_base, const Geom &g, 
 
 // The sequence bases of one (b, h): token 0 of each input and of o.
 struct SeqBase {
-    const void *q, *k, *v, *g, *beta;
+    const void *q, *k, *v, *g;
+    const float *beta;
     float *o;
 };
 
@@ -271,33 +313,40 @@ struct KRaw {
     float beta;
 };
 
+// The k-side loads q, k, g and beta with plain global loads (a wave-uniform
+// chunk base plus per-lane 32-bit offsets): on this part, buffer loads of the
+// same addresses hit the L2 less often when the four value slices of a head
+// read them, and cost about a third more HBM reads.  In a last, partial chunk
+// the token index of the offsets is clamped to the last token, so the loads
+// never leave the sequence.
 struct KOff {
     uint32_t tok;   // token n, channel 32 kw + 4 g (elements)
     uint32_t beta;  // token n (elements of beta)
 };
-__device__ __forceinline__ KOff kraw_offsets(const PrefillArgs &a, int tok, int kw, int grp) {
-    const int HD = static_cast<int>(a.H) * kD;
-    return KOff{static_cast<uint32_t>(tok * HD + 32 * kw + 4 * grp), static_cast<uint32_t>(tok * static_cast<int>(a.H))};
+__device__ __forceinline__ KOff kraw_offsets(int H, int tok, int kw, int grp) {
+    return KOff{static_cast<uint32_t>(tok * H * kD + 32 * kw + 4 * grp), static_cast<uint32_t>(tok * H)};
 }
 template <int G>  // GateMode
-__device__ __forceinline__ void load_kraw(KRaw &r, const SeqBase &sb, const Geom &gm, int c, const KOff &off) {
-    const Rsrc rq = chunk_rsrc<kD, 2>(sb.q, gm, c);
-    const Rsrc rk = chunk_rsrc<kD, 2>(sb.k, gm, c);
+__device__ __forceinline__ void load_kraw(KRaw &r, const SeqBase &sb, const Geom &gm, int c, const KOff &full,
+                                          int n16, int kw, int grp) {
+    const int64_t c0 = static_cast<int64_t>(c) * (kC * gm.H);  // first token row of chunk c (wave uniform)
+    KOff off = full;
+    if (c == gm.nlast && gm.tail < kC) off = kraw_offsets(gm.H, min(n16, gm.tail - 1), kw, grp);
+    constexpr int gsz = G == kGateLogitBf16 ? 2 : 4;
+    const char *qb = static_cast<const char *>(sb.q) + 2 * kD * c0;
+    const char *kb = static_cast<const char *>(sb.k) + 2 * kD * c0;
+    const char *gb = static_cast<const char *>(sb.g) + gsz * kD * c0;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
         const uint32_t e = off.tok + 16u * tt;
-        r.q[tt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rq, 2u * e, 0, 0));
-        r.k[tt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, 2u * e, 0, 0));
-        if constexpr (G == kGateLogitBf16) {
-            const Rsrc rg = chunk_rsrc<kD, 2>(sb.g, gm, c);
-            r.gx[tt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, 2u * e, 0, 0));
-        } else {
-            const Rsrc rg = chunk_rsrc<kD, 4>(sb.g, gm, c);
-            r.g[tt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, 4u * e, 0, 0));
-        }
+        r.q[tt] = *reinterpret_cast<const u32x2 *>(qb + 2u * e);
+        r.k[tt] = *reinterpret_cast<const u32x2 *>(kb + 2u * e);
+        if constexpr (G == kGateLogitBf16)
+            r.gx[tt] = *reinterpret_cast<const u32x2 *>(gb + 2u * e);
+        else
+            r.g[tt] = *reinterpret_cast<const f32x4 *>(gb + 4u * e);
     }
-    const Rsrc rb = chunk_rsrc<1, 4>(sb.beta, gm, c);
-    r.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4u * off.beta, 0, 0));
+    r.beta = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(sb.beta + c0) + 4u * off.beta);
 }
 
 // What a launch reads and writes: the full prefill, or one of the passes of
@@ -700,7 +749,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
 
     if (tid < 4) (&sm.flag[0][0])[tid] = 0u;
 
-    const KOff koff = kraw_offsets(a, n16, kw, grp);
+    const KOff koff = kraw_offsets(static_cast<int>(a.H), n16, kw, grp);
     // a state lane's token 4 grp + i, column col of o: element offset
     // voff0 + i HD within a chunk (the row step HD is wave uniform)
     const uint32_t HD = static_cast<uint32_t>(a.H) * kD;
@@ -720,8 +769,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
 
     if (kwave) {
         if (nchunks > 0) {
-            load_kraw<G>(raw[0], sb, gm, 0, koff);
-            load_kraw<G>(raw[1], sb, gm, min(1, nlast), koff);
+            load_kraw<G>(raw[0], sb, gm, 0, koff, n16, kw, grp);
+            load_kraw<G>(raw[1], sb, gm, min(1, nlast), koff, n16, kw, grp);
         }
     } else if (swave) {
 #pragma unroll
@@ -748,7 +797,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             if constexpr (decltype(kside_tag)::value) kside_in<G>(a, raw[PAR], in, (n + 2) * kC, n16);
             if constexpr (decltype(kside_tag)::value) {
                 kside(sm.ops[kslot], sm.gram[PAR], sm.beta[PAR], in, kw, grp, n16, lane);
-                load_kraw<G>(raw[PAR], sb, gm, min(static_cast<int>(n) + 4, nlast), koff);
+                load_kraw<G>(raw[PAR], sb, gm, min(static_cast<int>(n) + 4, nlast), koff, n16, kw, grp);
             }
             kslot = (kslot == kRing - 1) ? 0 : kslot + 1;
         });
@@ -756,13 +805,30 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
         int vslot = 2;  // ring slot of chunk n + 1 (n = -2 maps to slot 2)
         uint32_t v2 = 0;  // this lane's values of chunk n + 1, loaded one step ahead
         if (MODE != kNoValue && nchunks > 0) v2 = load_v2(sb, gm, 0, vb0);
+        // solver wave 0 paces this slice against the other slices of its (b, h)
+        const bool pace = a.epoch != 0 && sv == 0 && BH * kNV <= kPaceSlots;
+        uint64_t *pace_e = g_pace + (pace ? bh * kNV : 0);
+        uint64_t rep = ~0ull;  // the reports read at the last report step
         run_steps(nchunks, [&](auto par_tag, auto solve_tag, auto, auto, int64_t n) {
             constexpr int PAR = decltype(par_tag)::value;  // n & 1
             if constexpr (decltype(solve_tag)::value) {
-                if constexpr (MODE != kNoValue) {
-                    stage_v2(sm.ops[vslot], v2, sv, lane);
-                    v2 = load_v2(sb, gm, min(static_cast<int>(n) + 2, nlast), vb0);
+                if constexpr (MODE != kNoValue) stage_v2(sm.ops[vslot], v2, sv, lane);
+                if (pace && n % kPaceEvery == 1) {
+                    int64_t lead = pace_lead(rep, a.epoch, n, nv, lane);
+                    for (int spin = 0; lead > kPaceEvery + kPaceLead && spin < kPaceSpin; ++spin) {
+                        __builtin_amdgcn_s_sleep(4);
+                        lead = pace_lead(pace_read(pace_e, lane), a.epoch, n, nv, lane);
+                    }
                 }
+                // the reports are read before this step's value load, so the
+                // next step's wait for those values covers them as well
+                if (pace && n % kPaceEvery == 0) {
+                    if (lane == 0)
+                        __hip_atomic_store(pace_e + nv, (static_cast<uint64_t>(a.epoch) << 32) | static_cast<uint32_t>(n),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    rep = pace_read(pace_e, lane);
+                }
+                if constexpr (MODE != kNoValue) v2 = load_v2(sb, gm, min(static_cast<int>(n) + 2, nlast), vb0);
                 solve(sm.gram[PAR ^ 1], sm.beta[PAR ^ 1], sm.arow[sv], sm.ops[vslot].Mhl, sm.ops[vslot].P, sv, grp,
                       n16, lane);
             }
@@ -824,7 +890,11 @@ bool prefill_mfma_supported(const PrefillArgs &a) {
     return !(env && env[0] == '1');
 }
 
-hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s) {
+hipError_t launch_prefill_mfma(const PrefillArgs &args, hipStream_t s) {
+    static std::atomic<uint32_t> epochs{0};
+    PrefillArgs a = args;
+    a.epoch = epochs.fetch_add(1, std::memory_order_relaxed) + 1;
+    if (a.epoch == 0) a.epoch = epochs.fetch_add(1, std::memory_order_relaxed) + 1;  // (0 means unpaced)
     const int64_t BH = a.B * a.H;
     const int64_t rounds = (BH + 7) / 8;
     const dim3 grid(static_cast<unsigned>(rounds * 8 * kNV));
