@@ -4,7 +4,7 @@ Inputs are three rocprofv3 output directories made with the commands below
 (each one a separate run; counters never share a run with other tracing):
 
   rocprofv3 --kernel-trace --stats --output-format csv -d DIR_T -o trace -- \\
-      python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --segments 0
+      python3 bench.py --steps 20 --warmup 1 --no-cpu-baseline --segments 0
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR_F -o fetch -- \\
       python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --copy-calibration
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR_W -o write -- \\
@@ -104,7 +104,7 @@ def main(dt, df, dw, out):
              "the fused gate prologue) and decode (B=256 H=56 d=128)", "",
              "Commands (from the repository root):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d DIR_T -o trace -- "
-             "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --segments 0",
+             "python3 bench.py --steps 20 --warmup 1 --no-cpu-baseline --segments 0",
              "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR_F -o fetch -- "
              "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --copy-calibration",
              "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR_W -o write -- "
@@ -144,7 +144,7 @@ def segmented(dt, out, n_seg):
     """Kernel-trace summary of ``bench.py --segmented-only`` (the segmented prefill alone)."""
     stats = _csv(dt, "kernel_stats.csv")
     cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d DIR_T -o trace -- "
-           "python3 bench.py --segmented-only --segments %d --steps 5" % n_seg)
+           "python3 bench.py --segmented-only --segments %d --steps 10" % n_seg)
     lines = ["# rocprofv3: segmented KDA prefill (B=1 H=7 T=262144 d=128, %d segments)" % n_seg, "",
              "Commands (from the repository root):", "", "    " + cmd,
              "    python3 bench_traffic.py --segmented %d DIR_T profiles" % n_seg, "",
