@@ -129,6 +129,21 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t &hi, uin
     hi = __builtin_bit_cast(uint32_t, h);
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){l0, l1}, bf16x2));
 }
+// split8 that leaves the fp32 remainders x - hi in x (the state keeps them;
+// the hi halves come back through an identity product).
+__device__ __forceinline__ Sp8 split8_keep(float (&x)[8]) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const bf16x2 hh = __builtin_convertvector((f32x2){x[2 * p], x[2 * p + 1]}, bf16x2);
+        x[2 * p] = __builtin_amdgcn_fdot2_f32_bf16(hh, sgpr_pair(0x0000bf80u), x[2 * p], false);
+        x[2 * p + 1] = __builtin_amdgcn_fdot2_f32_bf16(hh, sgpr_pair(0xbf800000u), x[2 * p + 1], false);
+        h[p] = __builtin_bit_cast(uint32_t, hh);
+        l[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x[2 * p], x[2 * p + 1]}, bf16x2));
+    }
+    return Sp8{__builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]}),
+               __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]})};
+}
 __device__ __forceinline__ Sp4 split4(f32x4 x) {
     uint32_t h0, h1, l0, l1;
     split_pair(x[0], x[1], h0, l0);
@@ -575,19 +590,28 @@ template <int MODE>
 __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, const Ops &op, const Ops &nx, int64_t n,
                                             const SeqBase &sb, const Geom &gm, f32x4 (&S)[4],
                                             const SOps &cur, SOps &nxt, int rh, int ct, int grp, int n16, int lane,
-                                            uint32_t ob0, uint32_t so) {
+                                            uint32_t ob0, uint32_t so, bf16x4 ident) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const Sp4 Mf = Sp4{op.Mhl[0][lane], op.Mhl[1][lane]};
     const Sp4 Pf = Sp4{op.P[0][lane], op.P[1][lane]};
 
     // partial X = Kb S0 and Y = Qb S0 over this wave's 64 channels; the state
-    // rows of tiles 2js, 2js + 1 are the channels of operand slots 0..3, 4..7
+    // rows of tiles 2js, 2js + 1 are the channels of operand slots 0..3, 4..7.
+    // The split leaves S0 - hi in S; the hi halves are kept packed, and the
+    // update adds them back with an identity product.
     f32x4 X = zero, Y = zero;
+    bf16x8 Shi[2];
 #pragma unroll
     for (int js = 0; js < 2; ++js) {
-        const float sv[8] = {S[2 * js][0],     S[2 * js][1],     S[2 * js][2],     S[2 * js][3],
-                             S[2 * js + 1][0], S[2 * js + 1][1], S[2 * js + 1][2], S[2 * js + 1][3]};
-        const Sp8 Sb = split8(sv);
+        float sv[8] = {S[2 * js][0],     S[2 * js][1],     S[2 * js][2],     S[2 * js][3],
+                       S[2 * js + 1][0], S[2 * js + 1][1], S[2 * js + 1][2], S[2 * js + 1][3]};
+        const Sp8 Sb = split8_keep(sv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            S[2 * js][i] = sv[i];
+            S[2 * js + 1][i] = sv[4 + i];
+        }
+        Shi[js] = Sb.hi;
         X = mm32(cur.Kb[js], Sb, X);
         Y = mm32(cur.Qb[js], Sb, Y);
     }
@@ -636,7 +660,8 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
     // whose e^gamma_C sits in component t of lane (4 (n / 4) + i, g)'s eq
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const f32x4 acc = mm16(cur.KhT[t], U, S[t]);
+        const bf16x4 hi = t & 1 ? last4(Shi[t >> 1]) : first4(Shi[t >> 1]);
+        const f32x4 acc = mm16(cur.KhT[t], U, mfma16(ident, hi, S[t]));  // S0 = hi + (S0 - hi)
         S[t][0] = quad_bcast<0>(cur.eq[t]) * acc[0];
         S[t][1] = quad_bcast<1>(cur.eq[t]) * acc[1];
         S[t][2] = quad_bcast<2>(cur.eq[t]) * acc[2];
@@ -839,6 +864,10 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
         // SIMD issues their instructions first, and the k-side and solver
         // waves (which work ahead) fill the remaining issue cycles
         __builtin_amdgcn_s_setprio(3);
+        // the 16 x 16 identity as an A operand: lane (m, kg) holds row m, columns 4 kg .. 4 kg + 3
+        bf16x4 ident;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ident[j] = static_cast<__bf16>(n16 == 4 * grp + j ? 1.f : 0.f);
         int sslot = 1;        // ring slot of chunk n (n = -2 maps to slot 1)
         SOps so[2];           // operands of the chunks of even and odd steps
         int64_t ck_left = a.ckpt_every, ck_i = 0;  // chunks to the next checkpoint, its index
@@ -847,7 +876,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             const int nslot = (sslot == kRing - 1) ? 0 : sslot + 1;  // chunk n + 1
             if constexpr (decltype(state_tag)::value) {
                 state_chunk<MODE>(a, sm, sm.ops[sslot], sm.ops[nslot], n, sb, gm, S, so[PAR], so[PAR ^ 1], rh, ct,
-                                  grp, n16, lane, 4u * voff0, 4u * HD);
+                                  grp, n16, lane, 4u * voff0, 4u * HD, ident);
                 if (CKPT && --ck_left == 0) {  // the state after (ck_i + 1) * ckpt_every chunks
                     if (ck_i < a.n_ckpt) {
                         float *ck = a.ckpt + ck_i * (BH * kD * kD) + sbase;
