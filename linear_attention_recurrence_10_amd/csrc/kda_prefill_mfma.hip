@@ -401,7 +401,8 @@ struct KIn {
 // M, hence their rows of U, so their (finite) q, k and v never contribute.
 // With gate logits, the log-decay g = g_min sigmoid(x) is formed here.
 template <int G>  // GateMode
-__device__ __forceinline__ void kside_in(const PrefillArgs &a, const KRaw &raw, KIn &in, int64_t t0, int n16) {
+__device__ __forceinline__ void kside_in(const PrefillArgs &a, const KRaw &raw, KIn &in, int c, const Geom &gm,
+                                         int n16) {
     in.beta = raw.beta;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -425,8 +426,8 @@ __device__ __forceinline__ void kside_in(const PrefillArgs &a, const KRaw &raw, 
             in.k[4 * tt + 2 * p + 1] = bf16_hi(kp);
         }
     }
-    if (t0 + kC > a.T) {  // last, partial chunk (wave-uniform test)
-        if (t0 + n16 >= a.T) {
+    if (c >= gm.nlast) {  // the last chunk, or one past the end (wave-uniform test)
+        if ((c - gm.nlast) * kC + n16 >= gm.tail) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) in.g[j] = 0.f;
             in.beta = 0.f;
@@ -819,7 +820,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             constexpr int PAR = decltype(par_tag)::value;  // n & 1
             // reload the raw buffer at the end, once the unpacked values are dead
             KIn in;
-            if constexpr (decltype(kside_tag)::value) kside_in<G>(a, raw[PAR], in, (n + 2) * kC, n16);
+            if constexpr (decltype(kside_tag)::value) kside_in<G>(a, raw[PAR], in, static_cast<int>(n) + 2, gm, n16);
             if constexpr (decltype(kside_tag)::value) {
                 kside(sm.ops[kslot], sm.gram[PAR], sm.beta[PAR], in, kw, grp, n16, lane);
                 load_kraw<G>(raw[PAR], sb, gm, min(static_cast<int>(n) + 4, nlast), koff, n16, kw, grp);
