@@ -19,6 +19,8 @@ are unchanged) and OUT/kda_prefill_64k_decode_b256_rocprof.md.
 usage: python3 bench_traffic.py DIR_T DIR_F DIR_W OUT
        python3 bench_traffic.py --segmented N_SEG DIR_T OUT   (trace summary of
            bench.py --segmented-only: OUT/kda_prefill_256k_h7_segmented_rocprof.md)
+       python3 bench_traffic.py --util DIR_U OUT   (issue and pipe utilisation of the
+           prefill from one counter run: OUT/kda_prefill_64k_util.md)
 """
 from __future__ import annotations
 
@@ -167,7 +169,58 @@ def segmented(dt, out, n_seg):
     print("\n".join(lines))
 
 
+UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_MFMA "
+                 "SQ_INSTS_SALU SQ_INSTS_LDS GRBM_GUI_ACTIVE")
+
+
+def utilisation(du, out, cus=256, simds_per_cu=4, xcds=8):
+    """Issue and pipe-busy summary of the plain prefill from one counter run:
+
+    rocprofv3 --pmc <UTIL_COUNTERS> --output-format csv -d DIR_U -o util -- \
+        python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --no-decode --gate-logits none
+    """
+    import collections
+    rows = _csv(du, "counter_collection.csv")
+    per = collections.defaultdict(list)
+    for r in rows:
+        if PREFILL in r["Kernel_Name"]:
+            per[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    m = {k: statistics.mean(v) for k, v in per.items()}
+    # GRBM_GUI_ACTIVE comes summed over the XCDs' instances; the busy ratios
+    # take one XCD's active cycles (the vendor's derived metrics use the max)
+    active = m["GRBM_GUI_ACTIVE"] / xcds
+    steps = 65536 // 16
+    wgs = 56 * 4
+    per_chunk_simd = lambda c: m[c] / (wgs * simds_per_cu * steps)
+    cmd = ("rocprofv3 --pmc %s --output-format csv -d DIR_U -o util -- python3 bench.py --steps 2 --warmup 1 "
+           "--no-cpu-baseline --segments 0 --no-decode --gate-logits none" % UTIL_COUNTERS)
+    lines = ["# rocprofv3: KDA prefill (B=1 H=56 T=65536 d=128) issue and pipe utilisation", "",
+             "Commands (from the repository root):", "", "    " + cmd,
+             "    python3 bench_traffic.py --util DIR_U profiles", "",
+             "Kernel source hash: prefill %s" % bench.source_hash(), "",
+             "| figure | value |", "|---|---|",
+             "| GPU active cycles per launch (GRBM_GUI_ACTIVE / %d XCDs) | %.4g |" % (xcds, active),
+             "| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (active x %d SIMDs)) | %.1f%% |" % (
+                 cus * simds_per_cu, 100.0 * m["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * cus * simds_per_cu)),
+             "| VALU busy (SQ_ACTIVE_INST_VALU / (active x %d CUs)) | %.1f%% |" % (
+                 cus, 100.0 * m["SQ_ACTIVE_INST_VALU"] / (active * cus)),
+             "| vector instructions per chunk and SIMD (SQ_INSTS_VALU, MFMA included) | %.0f |" % per_chunk_simd("SQ_INSTS_VALU"),
+             "| of which MFMA (SQ_INSTS_MFMA) | %.0f |" % per_chunk_simd("SQ_INSTS_MFMA"),
+             "| of which fp32 transcendental (SQ_INSTS_VALU_TRANS_F32) | %.0f |" % per_chunk_simd("SQ_INSTS_VALU_TRANS_F32"),
+             "| scalar instructions per chunk and SIMD (SQ_INSTS_SALU) | %.0f |" % per_chunk_simd("SQ_INSTS_SALU"),
+             "| LDS instructions per chunk and SIMD (SQ_INSTS_LDS) | %.0f |" % per_chunk_simd("SQ_INSTS_LDS"),
+             "", "Per chunk and SIMD: counts divided by 224 work-groups x 4 SIMDs x 4096 chunks (launch "
+             "prologue and epilogue included)."]
+    os.makedirs(out, exist_ok=True)
+    with open(os.path.join(out, "kda_prefill_64k_util.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
+    if len(sys.argv) == 4 and sys.argv[1] == "--util":
+        utilisation(sys.argv[2], sys.argv[3])
+        sys.exit(0)
     if len(sys.argv) == 5 and sys.argv[1] == "--segmented":
         segmented(sys.argv[3], sys.argv[4], int(sys.argv[2]))
         sys.exit(0)
