@@ -129,20 +129,33 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t &hi, uin
     hi = __builtin_bit_cast(uint32_t, h);
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){l0, l1}, bf16x2));
 }
-// split8 that leaves the fp32 remainders x - hi in x (the state keeps them;
-// the hi halves come back through an identity product).
-__device__ __forceinline__ Sp8 split8_keep(float (&x)[8]) {
-    uint32_t h[4], l[4];
+// The state between steps: S holds the fp32 remainders S - hi, Shi the
+// packed bf16 high halves (tile 2 js in the first four slots of Shi[js], tile
+// 2 js + 1 in the last four).  state_split forms that pair from a full S,
+// state_full the full value back.
+__device__ __forceinline__ void state_split(f32x4 (&S)[4], bf16x8 (&Shi)[2]) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const bf16x2 hh = __builtin_convertvector((f32x2){x[2 * p], x[2 * p + 1]}, bf16x2);
-        x[2 * p] = __builtin_amdgcn_fdot2_f32_bf16(hh, sgpr_pair(0x0000bf80u), x[2 * p], false);
-        x[2 * p + 1] = __builtin_amdgcn_fdot2_f32_bf16(hh, sgpr_pair(0xbf800000u), x[2 * p + 1], false);
-        h[p] = __builtin_bit_cast(uint32_t, hh);
-        l[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x[2 * p], x[2 * p + 1]}, bf16x2));
+    for (int js = 0; js < 2; ++js) {
+        float sv[8] = {S[2 * js][0],     S[2 * js][1],     S[2 * js][2],     S[2 * js][3],
+                       S[2 * js + 1][0], S[2 * js + 1][1], S[2 * js + 1][2], S[2 * js + 1][3]};
+        uint32_t h[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const bf16x2 hh = __builtin_convertvector((f32x2){sv[2 * p], sv[2 * p + 1]}, bf16x2);
+            sv[2 * p] = __builtin_amdgcn_fdot2_f32_bf16(hh, sgpr_pair(0x0000bf80u), sv[2 * p], false);
+            sv[2 * p + 1] = __builtin_amdgcn_fdot2_f32_bf16(hh, sgpr_pair(0xbf800000u), sv[2 * p + 1], false);
+            h[p] = __builtin_bit_cast(uint32_t, hh);
+        }
+        Shi[js] = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            S[2 * js][i] = sv[i];
+            S[2 * js + 1][i] = sv[4 + i];
+        }
     }
-    return Sp8{__builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]}),
-               __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]})};
+}
+__device__ __forceinline__ float state_full(const f32x4 (&S)[4], const bf16x8 (&Shi)[2], int t, int i) {
+    return S[t][i] + static_cast<float>(Shi[t >> 1][4 * (t & 1) + i]);
 }
 __device__ __forceinline__ Sp4 split4(f32x4 x) {
     uint32_t h0, h1, l0, l1;
@@ -589,7 +602,7 @@ __device__ __forceinline__ float quad_bcast(float x) {
 // `cur`), `nx` chunk n + 1's, whose operands are read into `nxt`.
 template <int MODE>
 __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, const Ops &op, const Ops &nx, int64_t n,
-                                            const SeqBase &sb, const Geom &gm, f32x4 (&S)[4],
+                                            const SeqBase &sb, const Geom &gm, f32x4 (&S)[4], bf16x8 (&Shi)[2],
                                             const SOps &cur, SOps &nxt, int rh, int ct, int grp, int n16, int lane,
                                             uint32_t ob0, uint32_t so, bf16x4 ident) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -598,21 +611,18 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
 
     // partial X = Kb S0 and Y = Qb S0 over this wave's 64 channels; the state
     // rows of tiles 2js, 2js + 1 are the channels of operand slots 0..3, 4..7.
-    // The split leaves S0 - hi in S; the hi halves are kept packed, and the
-    // update adds them back with an identity product.
+    // S0 arrives split (S0 - hi in S, hi packed in Shi, from the end of the
+    // previous step); the update adds hi back with an identity product.
     f32x4 X = zero, Y = zero;
-    bf16x8 Shi[2];
 #pragma unroll
     for (int js = 0; js < 2; ++js) {
-        float sv[8] = {S[2 * js][0],     S[2 * js][1],     S[2 * js][2],     S[2 * js][3],
-                       S[2 * js + 1][0], S[2 * js + 1][1], S[2 * js + 1][2], S[2 * js + 1][3]};
-        const Sp8 Sb = split8_keep(sv);
+        uint32_t l[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            S[2 * js][i] = sv[i];
-            S[2 * js + 1][i] = sv[4 + i];
+        for (int p = 0; p < 4; ++p) {
+            const int t = 2 * js + (p >> 1), i = 2 * (p & 1);
+            l[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){S[t][i], S[t][i + 1]}, bf16x2));
         }
-        Shi[js] = Sb.hi;
+        const Sp8 Sb{Shi[js], __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]})};
         X = mm32(cur.Kb[js], Sb, X);
         Y = mm32(cur.Qb[js], Sb, Y);
     }
@@ -668,6 +678,8 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
         S[t][2] = quad_bcast<2>(cur.eq[t]) * acc[2];
         S[t][3] = quad_bcast<3>(cur.eq[t]) * acc[3];
     }
+    // the next step's split of S happens here, at the end of this step
+    state_split(S, Shi);
     // the update is issued before the next chunk's Kh^T, e^gamma_C are read
     asm volatile("" ::"v"(S[0]), "v"(S[1]), "v"(S[2]), "v"(S[3]) : "memory");
     read_kh(nxt, nx, rh, grp, n16, lane);
@@ -791,7 +803,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     const int nlast = static_cast<int>(nchunks) - 1;
     const Geom gm{static_cast<int>(a.H), nlast, static_cast<int>(T - static_cast<int64_t>(nlast) * kC)};
     KRaw raw[2];
-    f32x4 S[4];  // state rows 64 rh + 16 t + 4 g + i, column `col`
+    f32x4 S[4];  // state rows 64 rh + 16 t + 4 g + i, column `col` (between steps: S - hi)
+    bf16x8 Shi[2];  // and its high halves (between steps)
 
     if (kwave) {
         if (nchunks > 0) {
@@ -807,6 +820,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
                 S[t][i] = a.h0 ? a.h0[sbase + row * kD + col] : 0.f;
             }
         }
+        state_split(S, Shi);
     }
 
     // Step n: the k-side waves prepare chunk n + 2, the solver waves solve
@@ -876,7 +890,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             constexpr int PAR = decltype(par_tag)::value;
             const int nslot = (sslot == kRing - 1) ? 0 : sslot + 1;  // chunk n + 1
             if constexpr (decltype(state_tag)::value) {
-                state_chunk<MODE>(a, sm, sm.ops[sslot], sm.ops[nslot], n, sb, gm, S, so[PAR], so[PAR ^ 1], rh, ct,
+                state_chunk<MODE>(a, sm, sm.ops[sslot], sm.ops[nslot], n, sb, gm, S, Shi, so[PAR], so[PAR ^ 1], rh, ct,
                                   grp, n16, lane, 4u * voff0, 4u * HD, ident);
                 if (CKPT && --ck_left == 0) {  // the state after (ck_i + 1) * ckpt_every chunks
                     if (ck_i < a.n_ckpt) {
@@ -884,7 +898,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) ck[(64 * rh + 16 * t + 4 * grp + i) * kD + col] = S[t][i];
+                            for (int i = 0; i < 4; ++i)
+                                ck[(64 * rh + 16 * t + 4 * grp + i) * kD + col] = state_full(S, Shi, t, i);
                         }
                     }
                     ++ck_i;
@@ -905,7 +920,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 64 * rh + 16 * t + 4 * grp + i;
-                a.hT[sbase + row * kD + col] = S[t][i];
+                a.hT[sbase + row * kD + col] = state_full(S, Shi, t, i);
             }
         }
     }
