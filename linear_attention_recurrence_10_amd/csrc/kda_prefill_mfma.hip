@@ -205,22 +205,24 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_move(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
 }
-template <int U>
-__device__ __forceinline__ float row_bcast(float x) {  // lane U of the row to the whole row
-    return dpp_move<0x150 + U>(x);
-}
 // Right-looking forward substitution for one column of (I + A)^-1: lane
 // (row r = n, group g) holds X[r][s] for one column s per 16-lane row.  At
 // pivot u every row subtracts A[r][u] times row u; row u of the same column
 // lives in lane u of the same 16-lane row, so a DPP broadcast replaces any LDS
 // traffic.  A is strictly lower triangular, so rows r <= u are unaffected
 // (A[r][u] = 0).
-// `nar` holds row n of -A, so each pivot is one multiply-add whose DPP
-// broadcast folds into the instruction.
+// `nar` holds row n of -A, so each pivot is one multiply-add with the
+// broadcast as its DPP source operand.  The compiler does not fold a
+// row_newbcast move into the multiply-add (it emits a separate move), so the
+// fused instruction is written out; the s_nop in front gives the two wait
+// states that a DPP read of a register written by the previous vector
+// instruction needs, which the compiler cannot see inside the asm.
 template <int U>
 __device__ __forceinline__ void tri_pivots(float &x, const float (&nar)[kC]) {
     if constexpr (U < kC - 1) {
-        x = __builtin_fmaf(row_bcast<U>(x), nar[U], x);
+        asm("s_nop 1\n\tv_fmac_f32_dpp %0, %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf"
+            : "+v"(x)
+            : "v"(nar[U]), "i"(U));
         tri_pivots<U + 1>(x, nar);
     }
 }
@@ -263,6 +265,11 @@ constexpr int kPaceSlots = 1 << 16;  // 4 per (b, h): launches with B H <= 16384
 constexpr int kPaceEvery = 8;
 constexpr int kPaceLead = 6;
 constexpr int kPaceSpin = 4096;
+// Per-role extras go to different SIMDs (wave w runs on SIMD w % 4): the O
+// products to the state waves on SIMDs 0 and 3, P to the solver wave on SIMD
+// 2, the pacing to the one on SIMD 1.
+constexpr int kPSolver = 2;
+constexpr int kPaceSolver = 1;
 __device__ uint64_t g_pace[kPaceSlots];
 
 // Reports of the slices of one (b, h): lane s < 4 reads slice s's entry.
@@ -545,8 +552,8 @@ __device__ __forceinline__ void solve(const f32x4 (&gr)[4][2][64], const float (
     const __bf16 ml = static_cast<__bf16>(m - static_cast<float>(mh));
     reinterpret_cast<__bf16 *>(&Mo[0][16 * kw + n16])[grp] = mh;
     reinterpret_cast<__bf16 *>(&Mo[1][16 * kw + n16])[grp] = ml;
-    // P (lower triangle with the diagonal) comes from solver wave 0 alone
-    if (kw == 0) {
+    // P (lower triangle with the diagonal) comes from one solver wave alone
+    if (kw == kPSolver) {
         f32x4 ps = gr[0][1][lane];
 #pragma unroll
         for (int ww = 1; ww < 4; ++ww) ps += gr[ww][1][lane];
@@ -608,6 +615,11 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const Sp4 Mf = Sp4{op.Mhl[0][lane], op.Mhl[1][lane]};
     const Sp4 Pf = Sp4{op.P[0][lane], op.P[1][lane]};
+    // this chunk's values are read with M and P, ahead of the handshake: LDS
+    // reads complete in order, so a read issued after the handshake would
+    // also wait for the next chunk's operand reads issued there
+    u32x2 vp = {0u, 0u};
+    if constexpr (MODE != kNoValue) vp = *reinterpret_cast<const u32x2 *>(&op.vt[16 * ct + (lane & 15)][4 * grp]);
 
     // partial X = Kb S0 and Y = Qb S0 over this wave's 64 channels; the state
     // rows of tiles 2js, 2js + 1 are the channels of operand slots 0..3, 4..7.
@@ -626,8 +638,11 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
         X = mm32(cur.Kb[js], Sb, X);
         Y = mm32(cur.Qb[js], Sb, Y);
     }
+    // the row half rh == ct forms O of column tile ct (waves 4 and 7, on
+    // SIMDs 0 and 3); the other half hands it its Y
+    const bool owave = rh == ct;
     sm.xy[rh][0][ct][lane] = X;
-    if (rh == 1) sm.xy[1][1][ct][lane] = Y;
+    if (!owave) sm.xy[rh][1][ct][lane] = Y;
     // Y is formed here in both halves (so that Qb dies before the next
     // chunk's operands land in other registers)
     asm volatile("" ::"v"(Y));
@@ -637,11 +652,13 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
     const uint32_t tag = static_cast<uint32_t>(n + 1);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __hip_atomic_store(&sm.flag[ct][rh], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    while (__hip_atomic_load(&sm.flag[ct][rh ^ 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != tag)
-        __builtin_amdgcn_s_sleep(1);
+    // (a poll is one LDS round trip; the partner is at most a few hundred
+    // cycles away, so the loop does not sleep between polls)
+    while (__hip_atomic_load(&sm.flag[ct][rh ^ 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != tag) {
+    }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     const f32x4 Xo = sm.xy[rh ^ 1][0][ct][lane];
-    const f32x4 Yo = sm.xy[1][1][ct][lane];  // row half 1's Y (used by row half 0)
+    const f32x4 Yo = sm.xy[rh ^ 1][1][ct][lane];  // the other half's Y (used by the O wave)
     // the next chunk's Kb, Qb replace this chunk's (dead after X, Y); issued
     // after the handshake so that no flag poll waits for them
     asm volatile("" ::: "memory");
@@ -650,7 +667,6 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
 
     f32x4 vv = zero;
     if constexpr (MODE != kNoValue) {
-        const u32x2 vp = *reinterpret_cast<const u32x2 *>(&op.vt[16 * ct + (lane & 15)][4 * grp]);
         vv[0] = __uint_as_float(vp[0] << 16);
         vv[1] = __uint_as_float(vp[0] & 0xffff0000u);
         vv[2] = __uint_as_float(vp[1] << 16);
@@ -658,7 +674,7 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
     }
     const Sp4 U = split4(mm16(Mf, split4(vv - X), zero));
 
-    if (rh == 0 && MODE == kFull) {
+    if (owave && MODE == kFull) {
         const f32x4 O = mm16(Pf, U, Y + Yo);
         // o has the layout of v: token 4g + i, column `col` at byte offset ob0 + i so
         const Rsrc ro = chunk_rsrc<kD, 4>(sb.o, gm, static_cast<int>(n));
@@ -846,7 +862,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
         uint32_t v2 = 0;  // this lane's values of chunk n + 1, loaded one step ahead
         if (MODE != kNoValue && nchunks > 0) v2 = load_v2(sb, gm, 0, vb0);
         // solver wave 0 paces this slice against the other slices of its (b, h)
-        const bool pace = a.epoch != 0 && sv == 0 && BH * kNV <= kPaceSlots;
+        const bool pace = a.epoch != 0 && sv == kPaceSolver && BH * kNV <= kPaceSlots;
         uint64_t *pace_e = g_pace + (pace ? bh * kNV : 0);
         uint64_t rep = ~0ull;  // the reports read at the last report step
         run_steps(nchunks, [&](auto par_tag, auto solve_tag, auto, auto, int64_t n) {
