@@ -69,6 +69,26 @@ def calibration_copy(disp):
     return disp[max(copies)][1]
 
 
+TIMED_STEPS = 20  # --steps of the trace command
+
+
+def timed_means(dt, names):
+    """{kernel name (as in the stats): (mean ns, n)} over each kernel's last
+    TIMED_STEPS dispatches in the kernel trace."""
+    durs = {}
+    for r in _csv(dt, "kernel_trace.csv"):
+        name = r["Kernel_Name"][:90]
+        if name in names:
+            durs.setdefault(name, []).append((int(r["Dispatch_Id"]),
+                                              int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out = {}
+    for name, v in durs.items():
+        v.sort()
+        last = [d for _, d in v[-TIMED_STEPS:]]
+        out[name] = (statistics.mean(last), len(last))
+    return out
+
+
 def mean_for(disp, key):
     vals = [v for name, v in disp.values() if key in name]
     return statistics.mean(vals) if vals else None, len(vals)
@@ -97,6 +117,12 @@ def main(dt, df, dw, out):
                             "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])}
                            for r in stats if "prefill_mfma_kernel" in r["Name"] or DECODE in r["Name"]
                            or COPY in r["Name"]]
+    # the launches bench.py times with events (the last TIMED_STEPS of each
+    # kernel; the first is the warmup, whose cold start the --stats average
+    # includes): their mean is the figure comparable with the bench line
+    timed = timed_means(dt, [r["name"] for r in res["kernel_stats"]])
+    for r in res["kernel_stats"]:
+        r["timed_avg_ns"], r["timed_calls"] = timed.get(r["name"], (None, 0))
     os.makedirs(out, exist_ok=True)
     with open(os.path.join(out, "kda_prefill_64k_traffic.json"), "w") as f:
         json.dump(res, f, indent=1)
@@ -113,10 +139,15 @@ def main(dt, df, dw, out):
              "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --copy-calibration",
              "    python3 bench_traffic.py DIR_T DIR_F DIR_W profiles", "",
              "Kernel source hash: prefill %s, decode %s" % (res["kernel_src_sha"], res["decode_src_sha"]), "",
-             "## Kernel trace (--stats)", "", "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+             "## Kernel trace (--stats)", "",
+             "The last column is the mean over the last %d launches of each kernel (the ones bench.py times; "
+             "the first launch is its warmup)." % TIMED_STEPS, "",
+             "| kernel | calls | avg us | min us | max us | timed avg us |", "|---|---|---|---|---|---|"]
     for r in res["kernel_stats"]:
-        lines.append("| %s | %d | %.1f | %.1f | %.1f |" % (r["name"], r["calls"], r["avg_ns"] / 1e3,
-                                                          r["min_ns"] / 1e3, r["max_ns"] / 1e3))
+        t = r["timed_avg_ns"]
+        lines.append("| %s | %d | %.1f | %.1f | %.1f | %s |" % (r["name"], r["calls"], r["avg_ns"] / 1e3,
+                                                               r["min_ns"] / 1e3, r["max_ns"] / 1e3,
+                                                               "%.1f" % (t / 1e3) if t else "-"))
     lines += ["", "## HBM traffic (FETCH_SIZE, WRITE_SIZE)", "",
               "Copy calibration: %d bytes copied; raw FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB; "
               "scale factors %.4f (fetch), %.4f (write)." % (bench.COPY_BYTES, copy_f, copy_w, sf, sw), "",
