@@ -361,7 +361,8 @@ struct KOff {
 __device__ __forceinline__ KOff kraw_offsets(int H, int tok, int kw, int grp) {
     return KOff{static_cast<uint32_t>(tok * H * kD + 32 * kw + 4 * grp), static_cast<uint32_t>(tok * H)};
 }
-template <int G>  // GateMode
+// QS: the launch needs q (the passes without o do not read it).
+template <int G, bool QS>  // GateMode
 __device__ __forceinline__ void load_kraw(KRaw &r, const SeqBase &sb, const Geom &gm, int c, const KOff &full,
                                           int n16, int kw, int grp) {
     const int64_t c0 = static_cast<int64_t>(c) * (kC * gm.H);  // first token row of chunk c (wave uniform)
@@ -374,7 +375,7 @@ __device__ __forceinline__ void load_kraw(KRaw &r, const SeqBase &sb, const Geom
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
         const uint32_t e = off.tok + 16u * tt;
-        r.q[tt] = *reinterpret_cast<const u32x2 *>(qb + 2u * e);
+        if constexpr (QS) r.q[tt] = *reinterpret_cast<const u32x2 *>(qb + 2u * e);
         r.k[tt] = *reinterpret_cast<const u32x2 *>(kb + 2u * e);
         if constexpr (G == kGateLogitBf16)
             r.gx[tt] = *reinterpret_cast<const u32x2 *>(gb + 2u * e);
@@ -420,7 +421,7 @@ struct KIn {
 // set to 0 and their beta to 0.  That zeroes their rows and columns of A and
 // M, hence their rows of U, so their (finite) q, k and v never contribute.
 // With gate logits, the log-decay g = g_min sigmoid(x) is formed here.
-template <int G>  // GateMode
+template <int G, bool QS>  // GateMode
 __device__ __forceinline__ void kside_in(const PrefillArgs &a, const KRaw &raw, KIn &in, int c, const Geom &gm,
                                          int n16) {
     in.beta = raw.beta;
@@ -439,7 +440,8 @@ __device__ __forceinline__ void kside_in(const PrefillArgs &a, const KRaw &raw, 
         }
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const uint32_t qp = raw.q[tt][p], kp = raw.k[tt][p];
+            // (without QS, q is never loaded; its unpacked values are dead)
+            const uint32_t qp = QS ? raw.q[tt][p] : 0u, kp = raw.k[tt][p];
             in.q[4 * tt + 2 * p] = bf16_lo(qp);
             in.q[4 * tt + 2 * p + 1] = bf16_hi(qp);
             in.k[4 * tt + 2 * p] = bf16_lo(kp);
@@ -457,6 +459,8 @@ __device__ __forceinline__ void kside_in(const PrefillArgs &a, const KRaw &raw, 
 
 // K-side, second part: this quarter's operands of the chunk go to `op` (LDS or
 // a shared slot in global memory), its partial Grams to `gr`, beta to `bt`.
+// Without QS (no o) neither Qb nor P is formed.
+template <bool QS>
 __device__ __forceinline__ void kside(Ops &op, f32x4 (&gr)[4][2][64], float (&bt)[kC], const KIn &in, int kw,
                                       int grp, int n16, int lane) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -493,9 +497,13 @@ __device__ __forceinline__ void kside(Ops &op, f32x4 (&gr)[4][2][64], float (&bt
         kb[j] = kv[j] * ep[j];
         kh[j] = kv[j] * em[j];
     }
+    // (without QS, Qb is never stored or used, so its products and split
+    // are dead code)
     const Sp8 Qb = split8(qb), Kb = split8(kb), Kh = split8(kh);
-    op.qk[0][kw][0][lane] = Qb.hi;
-    op.qk[0][kw][1][lane] = Qb.lo;
+    if constexpr (QS) {
+        op.qk[0][kw][0][lane] = Qb.hi;
+        op.qk[0][kw][1][lane] = Qb.lo;
+    }
     op.qk[1][kw][0][lane] = Kb.hi;
     op.qk[1][kw][1][lane] = Kb.lo;
     // Kh tiles token-major: token n, channels 4g .. 4g + 3 of the tile at
@@ -515,11 +523,12 @@ __device__ __forceinline__ void kside(Ops &op, f32x4 (&gr)[4][2][64], float (&bt
     // partial Grams over this quarter, transposed:
     // mm32(Kh, Kb)[m][n] = Kh_m . Kb_n = (Kb Kh^T)[n][m], so lane (n, g) gets row n, columns 4g + i
     gr[kw][0][lane] = mm32(Kh, Kb, zero);
-    gr[kw][1][lane] = mm32(Kh, Qb, zero);
+    if constexpr (QS) gr[kw][1][lane] = mm32(Kh, Qb, zero);
 }
 
 // M = (I + A)^-1 diag(beta) and P of the chunk whose Grams sit in the `par`
 // buffers: solver wave kw solves columns 4 kw .. 4 kw + 3, one per 16-lane row.
+template <bool QS>
 __device__ __forceinline__ void solve(const f32x4 (&gr)[4][2][64], const float (&bt)[kC], f32x4 (&arow)[kC][5],
                                       bf16x4 (&Mo)[2][64], bf16x4 (&Po)[2][64], int kw, int grp, int n16,
                                       int lane) {
@@ -553,7 +562,7 @@ __device__ __forceinline__ void solve(const f32x4 (&gr)[4][2][64], const float (
     reinterpret_cast<__bf16 *>(&Mo[0][16 * kw + n16])[grp] = mh;
     reinterpret_cast<__bf16 *>(&Mo[1][16 * kw + n16])[grp] = ml;
     // P (lower triangle with the diagonal) comes from one solver wave alone
-    if (kw == kPSolver) {
+    if (QS && kw == kPSolver) {
         f32x4 ps = gr[0][1][lane];
 #pragma unroll
         for (int ww = 1; ww < 4; ++ww) ps += gr[ww][1][lane];
@@ -575,11 +584,12 @@ struct SOps {
     Sp4 KhT[4];        // 16-channel tiles 4 rh + t, channel per lane
     f32x4 eq;          // e^gamma_C of channels 64 rh + 16 t + 4 g + (n & 3), t = 0..3
 };
+template <bool QS>
 __device__ __forceinline__ void read_kq(SOps &s, const Ops &op, int rh, int lane) {
 #pragma unroll
     for (int js = 0; js < 2; ++js) {
         s.Kb[js] = Sp8{op.qk[1][2 * rh + js][0][lane], op.qk[1][2 * rh + js][1][lane]};
-        s.Qb[js] = Sp8{op.qk[0][2 * rh + js][0][lane], op.qk[0][2 * rh + js][1][lane]};
+        if constexpr (QS) s.Qb[js] = Sp8{op.qk[0][2 * rh + js][0][lane], op.qk[0][2 * rh + js][1][lane]};
     }
 }
 // Transposing LDS read (gfx950): inside each group of 16 lanes, lane i
@@ -612,6 +622,7 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
                                             const SeqBase &sb, const Geom &gm, f32x4 (&S)[4], bf16x8 (&Shi)[2],
                                             const SOps &cur, SOps &nxt, int rh, int ct, int grp, int n16, int lane,
                                             uint32_t ob0, uint32_t so, bf16x4 ident) {
+    constexpr bool QS = MODE == kFull;  // Y and O only where o is written
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const Sp4 Mf = Sp4{op.Mhl[0][lane], op.Mhl[1][lane]};
     const Sp4 Pf = Sp4{op.P[0][lane], op.P[1][lane]};
@@ -636,16 +647,16 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
         }
         const Sp8 Sb{Shi[js], __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]})};
         X = mm32(cur.Kb[js], Sb, X);
-        Y = mm32(cur.Qb[js], Sb, Y);
+        if constexpr (QS) Y = mm32(cur.Qb[js], Sb, Y);
     }
     // the row half rh == ct forms O of column tile ct (waves 4 and 7, on
     // SIMDs 0 and 3); the other half hands it its Y
     const bool owave = rh == ct;
     sm.xy[rh][0][ct][lane] = X;
-    if (!owave) sm.xy[rh][1][ct][lane] = Y;
+    if (QS && !owave) sm.xy[rh][1][ct][lane] = Y;
     // Y is formed here in both halves (so that Qb dies before the next
     // chunk's operands land in other registers)
-    asm volatile("" ::"v"(Y));
+    if constexpr (QS) asm volatile("" ::"v"(Y));
     // hand the partials to the other row half of this column tile and wait
     // for its own: its flag reaches n + 1 in this chunk and cannot move
     // further before the next work-group barrier
@@ -658,11 +669,12 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     const f32x4 Xo = sm.xy[rh ^ 1][0][ct][lane];
-    const f32x4 Yo = sm.xy[rh ^ 1][1][ct][lane];  // the other half's Y (used by the O wave)
+    f32x4 Yo = zero;  // the other half's Y (used by the O wave)
+    if constexpr (QS) Yo = sm.xy[rh ^ 1][1][ct][lane];
     // the next chunk's Kb, Qb replace this chunk's (dead after X, Y); issued
     // after the handshake so that no flag poll waits for them
     asm volatile("" ::: "memory");
-    read_kq(nxt, nx, rh, lane);
+    read_kq<QS>(nxt, nx, rh, lane);
     X += Xo;
 
     f32x4 vv = zero;
@@ -772,6 +784,7 @@ __device__ __forceinline__ void run_steps(int64_t nchunks, Body &&body) {
 template <bool CKPT, int G, int MODE>  // G: GateMode
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     __shared__ Smem sm;
+    constexpr bool QS = MODE == kFull;  // q, Qb, P and Y are needed only where o is written
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -824,8 +837,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
 
     if (kwave) {
         if (nchunks > 0) {
-            load_kraw<G>(raw[0], sb, gm, 0, koff, n16, kw, grp);
-            load_kraw<G>(raw[1], sb, gm, min(1, nlast), koff, n16, kw, grp);
+            load_kraw<G, QS>(raw[0], sb, gm, 0, koff, n16, kw, grp);
+            load_kraw<G, QS>(raw[1], sb, gm, min(1, nlast), koff, n16, kw, grp);
         }
     } else if (swave) {
 #pragma unroll
@@ -850,10 +863,10 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             constexpr int PAR = decltype(par_tag)::value;  // n & 1
             // reload the raw buffer at the end, once the unpacked values are dead
             KIn in;
-            if constexpr (decltype(kside_tag)::value) kside_in<G>(a, raw[PAR], in, static_cast<int>(n) + 2, gm, n16);
+            if constexpr (decltype(kside_tag)::value) kside_in<G, QS>(a, raw[PAR], in, static_cast<int>(n) + 2, gm, n16);
             if constexpr (decltype(kside_tag)::value) {
-                kside(sm.ops[kslot], sm.gram[PAR], sm.beta[PAR], in, kw, grp, n16, lane);
-                load_kraw<G>(raw[PAR], sb, gm, min(static_cast<int>(n) + 4, nlast), koff, n16, kw, grp);
+                kside<QS>(sm.ops[kslot], sm.gram[PAR], sm.beta[PAR], in, kw, grp, n16, lane);
+                load_kraw<G, QS>(raw[PAR], sb, gm, min(static_cast<int>(n) + 4, nlast), koff, n16, kw, grp);
             }
             kslot = (kslot == kRing - 1) ? 0 : kslot + 1;
         });
@@ -885,7 +898,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
                     rep = pace_read(pace_e, lane);
                 }
                 if constexpr (MODE != kNoValue) v2 = load_v2(sb, gm, min(static_cast<int>(n) + 2, nlast), vb0);
-                solve(sm.gram[PAR ^ 1], sm.beta[PAR ^ 1], sm.arow[sv], sm.ops[vslot].Mhl, sm.ops[vslot].P, sv, grp,
+                solve<QS>(sm.gram[PAR ^ 1], sm.beta[PAR ^ 1], sm.arow[sv], sm.ops[vslot].Mhl, sm.ops[vslot].P, sv, grp,
                       n16, lane);
             }
             vslot = (vslot == kRing - 1) ? 0 : vslot + 1;
@@ -923,7 +936,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
                 }
             } else if constexpr (PAR == 1) {
                 // step -1: chunk 0 was prepared in step -2; read its operands for step 0
-                read_kq(so[0], sm.ops[nslot], rh, lane);
+                read_kq<QS>(so[0], sm.ops[nslot], rh, lane);
                 read_kh(so[0], sm.ops[nslot], rh, grp, n16, lane);
             }
             sslot = nslot;
