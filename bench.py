@@ -33,7 +33,8 @@ HBM_PEAK_GBPS = 8000.0
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_prefill_64k_traffic.json")
 _CSRC = os.path.join(ROOT, "linear_attention_recurrence_10_amd", "csrc")
-KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in ("kda_prefill_mfma.hip", "kda_internal.h")]
+KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in ("kda_prefill_mfma.h", "kda_prefill_mfma.hip", "kda_prefill_mfma_gate.hip",
+                                                     "kda_internal.h")]
 DECODE_SOURCES = [os.path.join(_CSRC, f) for f in ("kda_decode.hip", "kda_internal.h")]
 
 

@@ -46,6 +46,7 @@ struct DecodeArgs {
 // Each launcher returns hipSuccess or the launch error; all are asynchronous.
 hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_prefill_mfma_gate(const PrefillArgs &a, dim3 grid, hipStream_t s);  // gate-logit variants
 bool prefill_mfma_supported(const PrefillArgs &a);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 // Segmented prefill helpers (kda_kcp.hip).

@@ -1,0 +1,20 @@
+// kda_prefill_mfma_gate.hip -- launches of the chunked KDA prefill with the
+// gate given as its logit (fp32 or bf16), g = g_min sigmoid(x) formed in the
+// kernel.  A separate translation unit so that these variants keep the
+// default scheduling strategy, which orders their heavier k-side better than
+// the ILP-first strategy used for the others.
+#include "kda_prefill_mfma.h"
+
+namespace kda {
+
+hipError_t launch_prefill_mfma_gate(const PrefillArgs &a, dim3 grid, hipStream_t s) {
+    if (a.gate == kGateLogitF32)
+        hipLaunchKernelGGL((prefill_mfma_kernel<false, kGateLogitF32, kFull>), grid, dim3(kThreads), 0, s, a);
+    else if (a.gate == kGateLogitBf16)
+        hipLaunchKernelGGL((prefill_mfma_kernel<false, kGateLogitBf16, kFull>), grid, dim3(kThreads), 0, s, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace kda
