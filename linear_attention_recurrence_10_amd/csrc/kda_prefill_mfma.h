@@ -879,7 +879,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
         int vslot = 2;  // ring slot of chunk n + 1 (n = -2 maps to slot 2)
         uint32_t v2 = 0;  // this lane's values of chunk n + 1, loaded one step ahead
         if (MODE != kNoValue && nchunks > 0) v2 = load_v2(sb, gm, 0, vb0);
-        // solver wave 0 paces this slice against the other slices of its (b, h)
+        // one solver wave (kPaceSolver) paces this slice against the other slices of its (b, h)
         const bool pace = a.epoch != 0 && sv == kPaceSolver && BH * kNV <= kPaceSlots;
         uint64_t *pace_e = g_pace + (pace ? bh * kNV : 0);
         uint64_t rep = ~0ull;  // the reports read at the last report step
