@@ -91,7 +91,16 @@ constexpr int kD = 128;     // head dimension (d_k = d_v)
 constexpr int kDVS = 32;    // value columns per work-group
 constexpr int kNV = kD / kDVS;
 constexpr int kC = kChunk;  // 16
-constexpr int kThreads = 768;
+// k-side waves per SIMD, set per translation unit before this header is
+// included: 1 (one 32-channel quarter per k-side wave, 12 waves) or 2 (one
+// 16-channel tile per k-side wave, 16 waves: the second k-side wave of SIMD
+// s is wave 12 + s).
+#ifndef KDA_KSIDE_WAVES_PER_SIMD
+#define KDA_KSIDE_WAVES_PER_SIMD 1
+#endif
+constexpr int kKSW = KDA_KSIDE_WAVES_PER_SIMD;
+static_assert(kKSW == 1 || kKSW == 2, "one or two k-side waves per SIMD");
+constexpr int kThreads = 768 + 256 * (kKSW - 1);
 constexpr int kRing = 3;    // chunks of k-side operands in flight
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -245,7 +254,7 @@ struct Ops {
 
 struct Smem {
     Ops ops[kRing];               // chunks n, n + 1, n + 2
-    f32x4 gram[2][4][2][64];      // partial Grams [parity][k-side wave][A, P][lane]
+    f32x4 gram[2][4 * kKSW][2][64];  // partial Grams [parity][k-side wave][A, P][lane]
     float beta[2][kC];
     f32x4 arow[4][kC][5];         // summed, masked A per solver wave; rows padded to 80 bytes
     f32x4 xy[2][2][2][64];        // partial X, Y [row half][X, Y][column tile][lane]
@@ -364,7 +373,7 @@ struct KOff {
     uint32_t beta;  // token n (elements of beta)
 };
 __device__ __forceinline__ KOff kraw_offsets(int H, int tok, int kw, int grp) {
-    return KOff{static_cast<uint32_t>(tok * H * kD + 32 * kw + 4 * grp), static_cast<uint32_t>(tok * H)};
+    return KOff{static_cast<uint32_t>(tok * H * kD + (32 / kKSW) * kw + 4 * grp), static_cast<uint32_t>(tok * H)};
 }
 // QS: the launch needs q (the passes without o do not read it).
 template <int G, bool QS>  // GateMode
@@ -378,7 +387,7 @@ __device__ __forceinline__ void load_kraw(KRaw &r, const SeqBase &sb, const Geom
     const char *kb = static_cast<const char *>(sb.k) + 2 * kD * c0;
     const char *gb = static_cast<const char *>(sb.g) + gsz * kD * c0;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < 2 / kKSW; ++tt) {
         const uint32_t e = off.tok + 16u * tt;
         if constexpr (QS) r.q[tt] = *reinterpret_cast<const u32x2 *>(qb + 2u * e);
         r.k[tt] = *reinterpret_cast<const u32x2 *>(kb + 2u * e);
@@ -431,7 +440,7 @@ __device__ __forceinline__ void kside_in(const PrefillArgs &a, const KRaw &raw, 
                                          int n16) {
     in.beta = raw.beta;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < 2 / kKSW; ++tt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if constexpr (G == kGateLogDecay) {
@@ -466,7 +475,7 @@ __device__ __forceinline__ void kside_in(const PrefillArgs &a, const KRaw &raw, 
 // a shared slot in global memory), its partial Grams to `gr`, beta to `bt`.
 // Without QS (no o) neither Qb nor P is formed.
 template <bool QS>
-__device__ __forceinline__ void kside(Ops &op, f32x4 (&gr)[4][2][64], float (&bt)[kC], const KIn &in, int kw,
+__device__ __forceinline__ void kside(Ops &op, f32x4 (&gr)[4 * kKSW][2][64], float (&bt)[kC], const KIn &in, int kw,
                                       int grp, int n16, int lane) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const float(&gv)[8] = in.g;
@@ -531,16 +540,73 @@ __device__ __forceinline__ void kside(Ops &op, f32x4 (&gr)[4][2][64], float (&bt
     if constexpr (QS) gr[kw][1][lane] = mm32(Kh, Qb, zero);
 }
 
+// K-side with two k-side waves per SIMD: this wave's 16-channel tile kt (the
+// half kt % 2 of the quarter kt / 2) goes to `op` as slots
+// 4 (kt % 2) .. 4 (kt % 2) + 3 of the quarter's 8-wide operands (one 8-byte
+// write each), its partial Grams (over 16 channels) to `gr[kt]`.  The
+// unpacked inputs are the first four slots of `in`.
+template <bool QS>
+__device__ __forceinline__ void kside_tile(Ops &op, f32x4 (&gr)[4 * kKSW][2][64], float (&bt)[kC], const KIn &in,
+                                           int kt, int grp, int n16, int lane) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    float gam[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        gam[j] = in.g[j] * kLog2e;
+        asm("" : "+v"(gam[j]));  // keeps gam + dpp(gam) a DPP add (not a product folded into an fma)
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gam[j] += dpp_move<0x111>(gam[j]);  // row_shr:1
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gam[j] += dpp_move<0x112>(gam[j]);  // row_shr:2
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gam[j] += dpp_move<0x114>(gam[j]);  // row_shr:4
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gam[j] += dpp_move<0x118>(gam[j]);  // row_shr:8
+    f32x4 ep, em, qb, kb, kh;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        ep[j] = __builtin_amdgcn_exp2f(gam[j]);
+        em[j] = __builtin_amdgcn_exp2f(-gam[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        qb[j] = in.q[j] * ep[j];
+        kb[j] = in.k[j] * ep[j];
+        kh[j] = in.k[j] * em[j];
+    }
+    const Sp4 Qb = split4(qb), Kb = split4(kb), Kh = split4(kh);
+    const int kq = kt >> 1, half = kt & 1;
+    if constexpr (QS) {
+        reinterpret_cast<bf16x4 *>(&op.qk[0][kq][0][lane])[half] = Qb.hi;
+        reinterpret_cast<bf16x4 *>(&op.qk[0][kq][1][lane])[half] = Qb.lo;
+    }
+    reinterpret_cast<bf16x4 *>(&op.qk[1][kq][0][lane])[half] = Kb.hi;
+    reinterpret_cast<bf16x4 *>(&op.qk[1][kq][1][lane])[half] = Kb.lo;
+    op.kht[kt][0][4 * n16 + grp] = Kh.hi;
+    op.kht[kt][1][4 * n16 + grp] = Kh.lo;
+    if (n16 == kC - 1) {
+        // e^gamma_C: slot j of row g is channel 16 kt + 4 g + j: row half kt / 4, tile kt % 4, q = j
+#pragma unroll
+        for (int q = 0; q < 4; ++q) reinterpret_cast<float *>(&op.eq[kt >> 2][grp][q])[kt & 3] = ep[q];
+    }
+    if (kt == 0 && grp == 0) bt[n16] = in.beta;
+    // partial Grams over this tile, transposed (16x16x16 products: the same
+    // result layout as the quarter's 16x16x32 ones)
+    gr[kt][0][lane] = mm16(Kh, Kb, zero);
+    if constexpr (QS) gr[kt][1][lane] = mm16(Kh, Qb, zero);
+}
+
 // M = (I + A)^-1 diag(beta) and P of the chunk whose Grams sit in the `par`
 // buffers: solver wave kw solves columns 4 kw .. 4 kw + 3, one per 16-lane row.
 template <bool QS>
-__device__ __forceinline__ void solve(const f32x4 (&gr)[4][2][64], const float (&bt)[kC], f32x4 (&arow)[kC][5],
+__device__ __forceinline__ void solve(const f32x4 (&gr)[4 * kKSW][2][64], const float (&bt)[kC], f32x4 (&arow)[kC][5],
                                       bf16x4 (&Mo)[2][64], bf16x4 (&Po)[2][64], int kw, int grp, int n16,
                                       int lane) {
     // lane (row r = n, column group g): sum the partial Grams of row r, columns 4g .. 4g + 3
     f32x4 as = gr[0][0][lane];
 #pragma unroll
-    for (int ww = 1; ww < 4; ++ww) as += gr[ww][0][lane];
+    for (int ww = 1; ww < 4 * kKSW; ++ww) as += gr[ww][0][lane];
     const float nbeta_r = -bt[n16];
     f32x4 av;  // row r of -A
 #pragma unroll
@@ -570,7 +636,7 @@ __device__ __forceinline__ void solve(const f32x4 (&gr)[4][2][64], const float (
     if (QS && kw == kPSolver) {
         f32x4 ps = gr[0][1][lane];
 #pragma unroll
-        for (int ww = 1; ww < 4; ++ww) ps += gr[ww][1][lane];
+        for (int ww = 1; ww < 4 * kKSW; ++ww) ps += gr[ww][1][lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ps[i] = (4 * grp + i <= n16) ? ps[i] : 0.f;
         const Sp4 pp = split4(ps);  // stored split: the state waves use it as is
@@ -811,9 +877,10 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     const int col0 = nv * kDVS;
     const int64_t sbase = bh * kD * kD;
 
-    const bool kwave = w < 4;
+    const bool kwave = w < 4 || (kKSW == 2 && w >= 12);
     const bool swave = w >= 4 && w < 8;
-    const int kw = w;              // k-side role: channel quarter
+    // k-side role: channel quarter (one k-side wave per SIMD) or 16-channel tile (two)
+    const int kw = kKSW == 1 ? w : (w < 4 ? 2 * w : 2 * (w - 12) + 1);
     const int rh = (w - 4) >> 1;   // state role: row half
     const int ct = (w - 4) & 1;    //             column tile
     const int sv = w - 8;          // solver role: columns 4 sv .. 4 sv + 3
@@ -870,7 +937,10 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             KIn in;
             if constexpr (decltype(kside_tag)::value) kside_in<G, QS>(a, raw[PAR], in, static_cast<int>(n) + 2, gm, n16);
             if constexpr (decltype(kside_tag)::value) {
-                kside<QS>(sm.ops[kslot], sm.gram[PAR], sm.beta[PAR], in, kw, grp, n16, lane);
+                if constexpr (kKSW == 1)
+                    kside<QS>(sm.ops[kslot], sm.gram[PAR], sm.beta[PAR], in, kw, grp, n16, lane);
+                else
+                    kside_tile<QS>(sm.ops[kslot], sm.gram[PAR], sm.beta[PAR], in, kw, grp, n16, lane);
                 load_kraw<G, QS>(raw[PAR], sb, gm, min(static_cast<int>(n) + 4, nlast), koff, n16, kw, grp);
             }
             kslot = (kslot == kRing - 1) ? 0 : kslot + 1;

@@ -1,8 +1,10 @@
 // kda_prefill_mfma_gate.hip -- launches of the chunked KDA prefill with the
 // gate given as its logit (fp32 or bf16), g = g_min sigmoid(x) formed in the
-// kernel.  A separate translation unit so that these variants keep the
-// default scheduling strategy, which orders their heavier k-side better than
-// the ILP-first strategy used for the others.
+// kernel.  A separate translation unit, so that these variants can take the
+// layout and the scheduling strategy that suit their heavier k-side (one
+// exponential and one reciprocal more per value): two k-side waves per SIMD,
+// each on one 16-channel tile, and the default strategy.
+#define KDA_KSIDE_WAVES_PER_SIMD 2
 #include "kda_prefill_mfma.h"
 
 namespace kda {
