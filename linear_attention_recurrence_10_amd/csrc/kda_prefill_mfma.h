@@ -36,6 +36,9 @@
 //    [32 kw, 32 kw + 32) of chunk n + 2 (gate prefix sums, exponentials, the
 //    scaled and split operands, its partial Grams).  Everything they produce
 //    goes to LDS: a ring of three chunks of operands, double-buffered Grams.
+//    A translation unit may set two k-side waves per SIMD instead (16 waves;
+//    waves 12..15 are the second ones): each then takes one 16-channel tile,
+//    half of a quarter, and the solvers sum eight partial Grams.
 //  * solver waves 8..11 sum the partial Grams of chunk n + 1 and solve
 //    (I + A) M = diag(beta), four columns each, and form P (double-buffered).
 //  * state waves 4..7 carry the state slice: wave (row half rh, column tile
