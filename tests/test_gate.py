@@ -122,3 +122,50 @@ def test_gate_64k_sampled():
     eh = rel_err(pick(hT, heads, cols, 1, 3), h_ref)
     say("gate 64k sampled: err_o=%.3e err_hT=%.3e" % (eo, eh))
     assert eo <= 2e-2 and eh <= 2e-2
+
+
+def test_gate_repeat_runs_are_bitwise_identical():
+    """The gate variants run with two k-side waves per SIMD and eight partial
+    Grams; their sum has a fixed order, so repeated launches agree bit for bit."""
+    x = kda_inputs.prefill_inputs(2, 300, 8, 128, "bf16", h0=True, seed=44, device=DEV, gate_logits="bf16")
+    say("case gate repeat")
+    o1, h1 = kda.chunk_fwd_gate(x["q"], x["k"], x["v"], x["x"], x["beta"], x["h0"])
+    o2, h2 = kda.chunk_fwd_gate(x["q"], x["k"], x["v"], x["x"], x["beta"], x["h0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+@pytest.mark.parametrize("T1", [16, 45])
+def test_gate_split_run_matches_single_run(T1):
+    """Resuming from a prefix's final state (prefix-cache reuse) gives the same
+    o and final state as one run over the whole sequence."""
+    T = 160
+    x = kda_inputs.prefill_inputs(1, T, 4, 128, "bf16", h0=True, seed=45, device=DEV, gate_logits="bf16")
+    say("case gate split %d" % T1)
+    o, hT = kda.chunk_fwd_gate(x["q"], x["k"], x["v"], x["x"], x["beta"], x["h0"])
+    part = {n: x[n][:, :T1].contiguous() for n in ("q", "k", "v", "x", "beta")}
+    rest = {n: x[n][:, T1:].contiguous() for n in ("q", "k", "v", "x", "beta")}
+    o1, h1 = kda.chunk_fwd_gate(part["q"], part["k"], part["v"], part["x"], part["beta"], x["h0"])
+    o2, h2 = kda.chunk_fwd_gate(rest["q"], rest["k"], rest["v"], rest["x"], rest["beta"], h1)
+    torch.cuda.synchronize()
+    assert rel_err(o1.cpu(), o[:, :T1].cpu()) < 1e-3
+    assert rel_err(o2.cpu(), o[:, T1:].cpu()) < 1e-3
+    assert rel_err(h2.cpu(), hT.cpu()) < 1e-3
+
+
+def test_gate_value_columns_are_independent():
+    """Changing value column j (and h0's column j) changes nothing in any other
+    column of o or the final state: the four 32-column slices and their two
+    column tiles each see only their own columns."""
+    x = kda_inputs.prefill_inputs(1, 70, 2, 128, "bf16", h0=True, seed=46, device=DEV, gate_logits="bf16")
+    say("case gate columns")
+    o1, h1 = kda.chunk_fwd_gate(x["q"], x["k"], x["v"], x["x"], x["beta"], x["h0"])
+    j = 77
+    v2, h02 = x["v"].clone(), x["h0"].clone()
+    v2[..., j] = -v2[..., j] + 0.5
+    h02[..., j] = 0.0
+    o2, h2 = kda.chunk_fwd_gate(x["q"], x["k"], v2, x["x"], x["beta"], h02)
+    torch.cuda.synchronize()
+    keep = [c for c in range(128) if c != j]
+    assert torch.equal(o1[..., keep], o2[..., keep]) and torch.equal(h1[..., keep], h2[..., keep])
+    assert not torch.equal(o1[..., j], o2[..., j])

@@ -135,3 +135,15 @@ def test_kcp_long_sequence_sampled():
     eh = rel_err(pick(hT, heads, cols, head_dim=1, col_dim=3), s_ref)
     say("  T=8192 P=16: o %.3e hT %.3e" % (eo, eh))
     assert eo <= tol_for("bf16") and eh <= tol_for("bf16")
+
+
+def test_kcp_repeat_runs_are_bitwise_identical():
+    """The three passes (the first two without o and without the q side) and
+    the scan give bit-identical results on a second launch with the same
+    workspace."""
+    x = kda_inputs.prefill_inputs(1, 1024, 3, 128, "bf16", h0=True, seed=77, device=DEV, gate_mean=SLOW)
+    say("case kcp repeat")
+    o1, h1 = run_kcp(x, 8, x["h0"])
+    o2, h2 = run_kcp(x, 8, x["h0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
