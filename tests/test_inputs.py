@@ -64,3 +64,20 @@ def test_decode_inputs_shapes():
 def test_rel_err():
     ref = torch.tensor([3.0, -4.0])
     assert abs(kda_inputs.rel_err(ref + torch.tensor([0.0, 0.5]), ref) - 0.5 / math.sqrt(12.5)) < 1e-12
+
+
+def test_generator_digests_are_recorded():
+    """The seeded CPU inputs hash to the digests recorded by
+    tests/golden/make_input_hashes.py: a change of torch's generators or of
+    the input recipe shows up here rather than as a shift in parity errors."""
+    import importlib.util
+
+    here = os.path.join(os.path.dirname(__file__), "golden")
+    spec = importlib.util.spec_from_file_location("make_input_hashes", os.path.join(here, "make_input_hashes.py"))
+    mk = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mk)
+    with open(os.path.join(here, "input_hashes.json")) as f:
+        want = json.load(f)
+    assert sorted(want) == sorted(mk.CASES)
+    for name, case in mk.CASES.items():
+        assert mk.digests(case) == want[name], name
