@@ -105,6 +105,7 @@ def cpu_baseline(target_s: float):
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": "first %d of %d tokens of the B=1 H=56 d=128 workload, all heads, fp64 token-sequential C "
                   "(OpenMP over heads), %.1f s wall" % (T, cfg.T, dt),
     }
@@ -152,6 +153,98 @@ def time_segmented(kda, torch, stream, n_seg, steps, single=True):
             "unit": "tokens/s"}
 
 
+def time_launches(torch, stream, fn, steps):
+    """Mean and min of `steps` event-timed launches of fn() on `stream` (after one untimed call)."""
+    fn()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record(stream)
+        fn()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in ev]
+    return sum(ms) / len(ms), min(ms)
+
+
+def time_configs(kda, torch, stream, names, steps):
+    """The other prefill workloads (parity cases of the same entry point), each
+    timed on its own inputs with its algorithmic bytes and roofline fraction.
+    Inputs are generated on the device and freed before the next workload."""
+    import kda_inputs
+
+    out = {}
+    for name in names:
+        cfg = kda_inputs.PREFILL_CONFIGS[name]
+        log("config %s" % name)
+        x = kda_inputs.config_inputs(cfg, device=torch.device("cuda:0"))
+        o = torch.empty((cfg.B, cfg.T, cfg.H, cfg.D), dtype=torch.float32, device="cuda:0")
+        hT = torch.empty((cfg.B, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device="cuda:0")
+        torch.cuda.synchronize()
+
+        def fn():
+            kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], o=o, hT=hT, stream=stream)
+
+        n = steps if cfg.B * cfg.T * cfg.H <= (1 << 22) else max(3, steps // 5)
+        avg, mn = time_launches(torch, stream, fn, n)
+        esz = 2 if cfg.dtype == "bf16" else 4
+        nbytes = prefill_bytes(cfg.B, cfg.T, cfg.H, cfg.D, esz, h0=cfg.h0, hT=True)
+        gbps = nbytes / (avg * 1e-3) / 1e9
+        out[name] = {"B": cfg.B, "H": cfg.H, "T": cfg.T, "d": cfg.D, "dtype": cfg.dtype, "h0": cfg.h0,
+                     "launches": n, "ms": avg, "min_ms": mn, "tokens_per_s": cfg.B * cfg.T / (avg * 1e-3),
+                     "alg_bytes_per_launch": nbytes, "achieved": gbps, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS}
+        del x, o, hT
+        torch.cuda.empty_cache()
+    return out
+
+
+def copy_bandwidth(torch, stream, nbytes=1 << 30, steps=10):
+    """A plain device-to-device copy of nbytes: the streaming rate this part
+    reaches (read + write bytes over time), context for the HBM fractions."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    avg, mn = time_launches(torch, stream, lambda: dst.copy_(src), steps)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * nbytes, "ms": avg, "achieved": 2 * nbytes / (avg * 1e-3) / 1e9, "unit": "GB/s",
+            "frac_of_peak": 2 * nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+
+
+def decode_host_cost(kda, torch, calls=200):
+    """Host microseconds per kda_decode_step call (argument checks and the
+    launch, no synchronisation) at a small batch, through the C ABI."""
+    import ctypes
+    import kda_inputs
+
+    d = kda_inputs.decode_inputs(1, 8, 128, "bf16", seed=3, device=torch.device("cuda:0"))
+    o = torch.empty((1, 8, 128), dtype=torch.float32, device="cuda:0")
+    lib = kda.library()
+    p = [ctypes.c_void_p(d[n].data_ptr()) for n in ("q", "k", "v", "g", "beta", "state")]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    args = p + [ctypes.c_void_p(o.data_ptr()), 1, 8, 128, 128, 1, ctypes.c_float(0.0), stream]
+    for _ in range(10):
+        lib.kda_decode_step(*args)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        st = lib.kda_decode_step(*args)
+    t1 = time.perf_counter()
+    torch.cuda.synchronize()
+    assert st == 0
+    return {"batch": "B=1 H=8 d=128 bf16", "calls": calls, "host_us_per_call": 1e6 * (t1 - t0) / calls}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +262,8 @@ def main():
                          "long 7-head sequence, beside the single pass (0 = skip)")
     ap.add_argument("--segmented-only", action="store_true",
                     help="time only the segmented prefill (for a kernel trace of its launches alone)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other prefill workloads (tiny, B=4 H=16 T=4096, T=2^20)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain device copy of %d bytes first (for the traffic counters)" % (1 << 30))
     args = ap.parse_args()
@@ -350,10 +445,20 @@ def main():
                                 "traffic": load_traffic("gate") if gate_dt == "bf16" else None}
     if seg is not None:
         result["segmented"] = seg
+    result["copy"] = copy_bandwidth(torch, stream)
+    if d is not None:
+        result["decode"]["host"] = decode_host_cost(kda, torch)
+    if not args.no_configs:
+        import kda_inputs
+        del d
+        torch.cuda.empty_cache()
+        result["configs"] = time_configs(kda, torch, stream, [kda_inputs.TINY.name, kda_inputs.PREFILL_B4.name,
+                                                                kda_inputs.PREFILL_1M.name], args.steps)
     if not args.no_cpu_baseline:
         del x, o, hT
         log("cpu baseline (oracle), ~%.0f s" % args.cpu_seconds)
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        result["cpu_baseline"]["gpu_over_cpu"] = result["value"] / result["cpu_baseline"]["value"]
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

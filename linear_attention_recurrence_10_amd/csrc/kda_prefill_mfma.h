@@ -344,7 +344,8 @@ __device__ __forceinline__ uint32_t span_rows(const Geom &g, int c) {
 template <int W, int ESZ>
 __device__ __forceinline__ Rsrc chunk_rsrc(const void *seq_base, const Geom &g, int c) {
     const char *p = static_cast<const char *>(seq_base) +
-                    static_cast<uint64_t>(static_cast<uint32_t>(c)) * static_cast<uint32_t>(kC * g.H * W * ESZ);
+                    static_cast<uint64_t>(static_cast<uint32_t>(c)) *
+                        (static_cast<uint32_t>(g.H) * static_cast<uint32_t>(kC * W * ESZ));
     return make_rsrc(p, span_rows(g, c) * (W * ESZ));
 }
 

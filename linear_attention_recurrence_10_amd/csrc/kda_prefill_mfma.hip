@@ -9,11 +9,18 @@
 
 namespace kda {
 
-bool prefill_mfma_supported(const PrefillArgs &a) {
-    // the kernel's 32-bit in-chunk byte offsets need 16 * H * 128 * 4 < 2^31
-    if (a.D != kD || !a.bf16 || a.H > 65536) return false;
+// KDA_DISABLE_MFMA=1 in the environment routes every prefill to the fp32
+// vector kernel (a comparison knob for tests); it is read once per process.
+static const bool g_mfma_disabled = [] {
     const char *env = getenv("KDA_DISABLE_MFMA");
-    return !(env && env[0] == '1');
+    return env && env[0] == '1';
+}();
+
+bool prefill_mfma_supported(const PrefillArgs &a) {
+    // the kernel's 32-bit in-chunk byte offsets need kC * H * 128 * 4 < 2^31,
+    // i.e. H < 65536 (the products are formed in 32 bits)
+    if (a.D != kD || !a.bf16 || a.H >= 65536) return false;
+    return !g_mfma_disabled;
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &args, hipStream_t s) {

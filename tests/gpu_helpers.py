@@ -56,3 +56,57 @@ def pick(t: torch.Tensor, heads, cols, head_dim=2, col_dim=3) -> torch.Tensor:
 
 
 rel_err = kda_inputs.rel_err
+
+
+class ErrAcc:
+    """One ``max|x - ref| / rms(ref)`` over a tensor that is compared in pieces.
+
+    ``add`` takes one piece (any shape) and keeps the running maximum of the
+    absolute error and the running sum of squares of the reference, so the
+    result equals ``rel_err`` of the whole tensor while only one piece is held
+    on the host at a time.
+    """
+
+    def __init__(self):
+        self.max_err = 0.0
+        self.sumsq = 0.0
+        self.n = 0
+
+    def add(self, x, ref) -> None:
+        x = torch.as_tensor(x).double().cpu()
+        ref = torch.as_tensor(ref).double().cpu()
+        assert x.shape == ref.shape, (x.shape, ref.shape)
+        if ref.numel() == 0:
+            return
+        self.max_err = max(self.max_err, float((x - ref).abs().max().item()))
+        self.sumsq += float(ref.pow(2).sum().item())
+        self.n += ref.numel()
+
+    def value(self) -> float:
+        rms = (self.sumsq / self.n) ** 0.5 if self.n else 0.0
+        return self.max_err / rms if rms > 0.0 else self.max_err
+
+
+def head_groups(H: int, per: int):
+    """Consecutive head index lists of at most ``per`` heads covering 0 .. H-1."""
+    return [list(range(h, min(H, h + per))) for h in range(0, H, per)]
+
+
+def oracle_heads(x: dict, heads, t0=0, t1=None, S0=None, g=None):
+    """Oracle over every value column of heads ``heads``, tokens [t0, t1).
+
+    S0 ([B, len(heads), Dk, Dv] fp64) is the initial state; when None,
+    x["h0"] of those heads is used (or zeros).  ``g`` overrides x["g"] (for the
+    gate-logit entry, whose log-decay the oracle forms itself).
+    Returns (o [B, t1-t0, len(heads), Dv], S [B, len(heads), Dk, Dv]) in fp64.
+    """
+    T = x["q"].shape[1]
+    t1 = T if t1 is None else t1
+    hi = torch.as_tensor(heads, device=x["q"].device)
+    sl = lambda t: t[:, t0:t1].index_select(2, hi)
+    q, k, v = (host64(sl(x[n])) for n in ("q", "k", "v"))
+    gg = host64(sl(x["g"])) if g is None else np.ascontiguousarray(g)
+    beta = host64(x["beta"][:, t0:t1].index_select(2, hi))
+    if S0 is None and x.get("h0") is not None:
+        S0 = host64(x["h0"].index_select(1, hi))
+    return oracle.kda_fwd(q, k, v, gg, beta, h0=S0)

@@ -82,3 +82,26 @@ def test_source_hash_tracks_the_kernel_sources():
     names = sorted(os.path.basename(f) for f in bench.KERNEL_SOURCES)
     assert names == ["kda_internal.h", "kda_prefill_mfma.h", "kda_prefill_mfma.hip", "kda_prefill_mfma_gate.hip"]
     assert bench.source_hash() == bench.source_hash(bench.KERNEL_SOURCES)
+
+
+def test_piecewise_error_equals_whole_tensor_error():
+    """The whole-tensor parity tests compare a tensor in pieces (head groups,
+    batch blocks); the accumulated max|err| / rms must equal the metric taken
+    over the whole tensor at once."""
+    import torch
+
+    import kda_inputs
+    from gpu_helpers import ErrAcc, head_groups
+
+    gen = torch.Generator().manual_seed(5)
+    ref = torch.randn(2, 33, 56, 8, generator=gen, dtype=torch.float64)
+    x = ref + 1e-3 * torch.randn(2, 33, 56, 8, generator=gen, dtype=torch.float64)
+    x[1, 7, 50, 3] += 0.5  # the worst element sits in the last group
+    acc = ErrAcc()
+    groups = head_groups(56, 28)
+    assert [len(g) for g in groups] == [28, 28] and sum(groups, []) == list(range(56))
+    for heads in head_groups(56, 20):
+        acc.add(x[:, :, heads], ref[:, :, heads])
+    whole = kda_inputs.rel_err(x, ref)
+    assert abs(acc.value() - whole) <= 1e-12 * whole
+    assert acc.n == ref.numel()
