@@ -23,8 +23,12 @@
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers on the calling thread's current
  *    HIP device, owned by the caller.  The library allocates no device
- *    memory and keeps no state between calls besides cached device
- *    properties.  Calls are thread-safe.
+ *    memory at run time.  It holds two fixed device arrays per device, which
+ *    come with the loaded library: 512 KB of progress reports that pace the
+ *    prefill's work-groups (no result depends on them) and the 32 MiB
+ *    workspace of kda_chunk_fwd_kcp_noalloc.  Besides these it keeps only
+ *    cached device properties.  Calls are thread-safe, except that
+ *    kda_chunk_fwd_kcp_noalloc calls overlapping on one device race.
  *  - Every call is asynchronous and ordered on `stream` (a hipStream_t passed
  *    as void*; NULL = the null stream).  The library never synchronises.
  *  - Layouts are dense, row-major, token-major:
@@ -182,6 +186,36 @@ kda_status kda_chunk_fwd_kcp(const void *q, const void *k, const void *v,
  * are invalid (non-positive, T not a multiple of n_seg, or 64-bit overflow).
  */
 uint64_t kda_chunk_fwd_kcp_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t n_seg);
+
+/*
+ * kda_chunk_fwd_kcp_noalloc -- kda_chunk_fwd_kcp for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation and results, with
+ * the workspace taken from a fixed array the library keeps on each device
+ * (kda_chunk_fwd_kcp_noalloc_max_bytes() bytes, 32 MiB, held until the process
+ * ends) instead of a `ws` argument.  The call allocates nothing.
+ *
+ *   - A request whose workspace (kda_chunk_fwd_kcp_ws_bytes(...)) exceeds the
+ *     array is KDA_ERR_UNSUPPORTED: 3 * B * n_seg * H * Dk * Dv * 4 bytes
+ *     must fit, e.g. B * n_seg * H <= 170 at Dk = Dv = 128.
+ *   - Every call on one device uses that device's one array, so calls that
+ *     overlap in time on one device (other streams, other threads) race and
+ *     give wrong results; calls ordered on one stream are safe.  Nothing in the
+ *     array needs to start at zero: each call writes all it reads.
+ *   - The array's address is looked up once per device, on the first call
+ *     made while that device is current.
+ *
+ * All other arguments, the layouts and the errors are those of
+ * kda_chunk_fwd_kcp.
+ */
+kda_status kda_chunk_fwd_kcp_noalloc(const void *q, const void *k, const void *v,
+                                     const float *g, const float *beta, const float *h0,
+                                     float *o, float *hT, int64_t n_seg,
+                                     int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                     kda_dtype in_dtype, float scale, void *stream);
+
+/* Size in bytes of kda_chunk_fwd_kcp_noalloc's fixed workspace array. */
+uint64_t kda_chunk_fwd_kcp_noalloc_max_bytes(void);
 
 /*
  * kda_decode_step -- one new token per sequence (recurrent decoding, the case

@@ -16,7 +16,7 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_ckpt", "chunk_fwd_gate", "chunk_fwd_kcp", "kcp_ws_bytes", "decode_step", "KdaError", "library", "library_path", "version"]
+__all__ = ["chunk_fwd", "chunk_fwd_ckpt", "chunk_fwd_gate", "chunk_fwd_kcp", "chunk_fwd_kcp_noalloc", "kcp_ws_bytes", "decode_step", "KdaError", "library", "library_path", "version"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -61,6 +61,11 @@ def library() -> ctypes.CDLL:
             lib.kda_chunk_fwd_kcp.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, i64, vp, ctypes.c_uint64,
                                               i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, vp]
             lib.kda_chunk_fwd_kcp.restype = ctypes.c_int
+            lib.kda_chunk_fwd_kcp_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, i64, i64, i64, i64, i64, i64,
+                                                      ctypes.c_int, ctypes.c_float, vp]
+            lib.kda_chunk_fwd_kcp_noalloc.restype = ctypes.c_int
+            lib.kda_chunk_fwd_kcp_noalloc_max_bytes.argtypes = []
+            lib.kda_chunk_fwd_kcp_noalloc_max_bytes.restype = ctypes.c_uint64
             lib.kda_chunk_fwd_kcp_ws_bytes.argtypes = [i64, i64, i64, i64, i64, i64]
             lib.kda_chunk_fwd_kcp_ws_bytes.restype = ctypes.c_uint64
             lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, i64, i64, i64, i64,
@@ -231,6 +236,40 @@ def chunk_fwd_kcp(q, k, v, g, beta, h0=None, *, n_seg: int, ws=None, scale: floa
     _check(lib.kda_chunk_fwd_kcp(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
                                  int(n_seg), _ptr(ws), ws_bytes, B, T, H, Dk, Dv, _dtype_code(q),
                                  float(scale or 0.0), _stream(stream)))
+    return o, hT
+
+
+def chunk_fwd_kcp_noalloc(q, k, v, g, beta, h0=None, *, n_seg: int, scale: float | None = None, o=None, hT=None,
+                          output_final_state: bool = True, stream=None):
+    """:func:`chunk_fwd_kcp` with the library's fixed per-device workspace
+    (``kda_chunk_fwd_kcp_noalloc``): the C call allocates nothing.  Pass ``o``
+    (and ``hT``) to keep this function allocation-free as well.  Calls that
+    overlap in time on one device race on that workspace."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.float32)
+    if hT is None and output_final_state:
+        hT = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if hT is not None:
+        _need(hT, "hT", torch.float32)
+    shapes_ok = (k.shape == q.shape and g.shape == q.shape and v.shape[:3] == (B, T, H)
+                 and beta.shape == (B, T, H) and o.shape == (B, T, H, Dv)
+                 and (h0 is None or h0.shape == (B, H, Dk, Dv))
+                 and (hT is None or hT.shape == (B, H, Dk, Dv)))
+    if not shapes_ok:
+        raise ValueError("inconsistent shapes")
+    lib = library()
+    _check(lib.kda_chunk_fwd_kcp_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o),
+                                         _ptr(hT), int(n_seg), B, T, H, Dk, Dv, _dtype_code(q),
+                                         float(scale or 0.0), _stream(stream)))
     return o, hT
 
 

@@ -252,10 +252,18 @@ uint64_t kda_chunk_fwd_kcp_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk,
     return n * 4;
 }
 
-kda_status kda_chunk_fwd_kcp(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                             const float *h0, float *o, float *hT, int64_t n_seg, void *ws, uint64_t ws_bytes,
-                             int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale,
-                             void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The segmented prefill.  `ws_fixed`: ws is the library's own per-device
+// scratch array (kda_chunk_fwd_kcp_noalloc), already known to be a device
+// buffer of ws_bytes that overlaps nothing; a request larger than it is
+// rejected as unsupported.
+kda_status chunk_fwd_kcp(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                         const float *h0, float *o, float *hT, int64_t n_seg, void *ws, uint64_t ws_bytes,
+                         bool ws_fixed, int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype,
+                         float scale, void *stream) {
     if (n_seg < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "n_seg=%lld must be >= 1", (long long)n_seg);
     const bool split = n_seg > 1 && T > 0;
     uint64_t need = 0;
@@ -265,6 +273,11 @@ kda_status kda_chunk_fwd_kcp(const void *q, const void *k, const void *v, const 
                         (long long)n_seg);
         need = kda_chunk_fwd_kcp_ws_bytes(B, T, H, Dk, Dv, n_seg);
         if (need == 0) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace size overflows 64 bits");
+        if (ws_fixed && need > ws_bytes)
+            return fail(KDA_ERR_UNSUPPORTED,
+                        "the segmented prefill needs %llu bytes of workspace; the fixed array holds %llu "
+                        "(3 * B * n_seg * H * Dk * Dv * 4 bytes must fit)",
+                        (unsigned long long)need, (unsigned long long)ws_bytes);
         if (!ws || ws_bytes < need)
             return fail(KDA_ERR_INVALID_ARGUMENT, "ws (%llu bytes) must hold %llu bytes",
                         (unsigned long long)ws_bytes, (unsigned long long)need);
@@ -285,11 +298,13 @@ kda_status kda_chunk_fwd_kcp(const void *q, const void *k, const void *v, const 
     const Span others[] = {{"q", q, n_tok * Dk * esz}, {"k", k, n_tok * Dk * esz}, {"v", v, n_tok * Dv * esz},
                            {"g", g, n_tok * Dk * 4},   {"beta", beta, n_tok * 4},  {"h0", h0, n_state * 4},
                            {"o", o, n_tok * Dv * 4},   {"hT", hT, n_state * 4}};
-    for (const Span &x : others) {
-        if (overlaps(wsp, x)) return fail(KDA_ERR_INVALID_ARGUMENT, "ws overlaps %s", x.name);
+    if (!ws_fixed) {
+        for (const Span &x : others) {
+            if (overlaps(wsp, x)) return fail(KDA_ERR_INVALID_ARGUMENT, "ws overlaps %s", x.name);
+        }
+        st = check_spans(&wsp, 1);
+        if (st != KDA_OK) return st;
     }
-    st = check_spans(&wsp, 1);
-    if (st != KDA_OK) return st;
 
     // segments as batch entries: [B, T, ...] is [B * n_seg, T / n_seg, ...]
     const int64_t L = T / n_seg, BP = B * n_seg;
@@ -325,6 +340,34 @@ kda_status kda_chunk_fwd_kcp(const void *q, const void *k, const void *v, const 
     fin.o = o;
     return launch_prefill(fin, s);
 }
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd_kcp(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                             const float *h0, float *o, float *hT, int64_t n_seg, void *ws, uint64_t ws_bytes,
+                             int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale,
+                             void *stream) {
+    return chunk_fwd_kcp(q, k, v, g, beta, h0, o, hT, n_seg, ws, ws_bytes, false, B, T, H, Dk, Dv, in_dtype, scale,
+                         stream);
+}
+
+kda_status kda_chunk_fwd_kcp_noalloc(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                                     const float *h0, float *o, float *hT, int64_t n_seg, int64_t B, int64_t T,
+                                     int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale,
+                                     void *stream) {
+    // the device check comes first: the scratch lookup needs a usable current device
+    kda_status st = check_device();
+    if (st != KDA_OK) return st;
+    void *ws = nullptr;
+    const hipError_t e = kda::kcp_scratch(&ws);
+    if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "scratch array lookup failed: %s", hipGetErrorString(e));
+    return chunk_fwd_kcp(q, k, v, g, beta, h0, o, hT, n_seg, ws, kda::kKcpScratchBytes, true, B, T, H, Dk, Dv,
+                         in_dtype, scale, stream);
+}
+
+uint64_t kda_chunk_fwd_kcp_noalloc_max_bytes(void) { return kda::kKcpScratchBytes; }
 
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
                            float *state, float *o, int64_t B, int64_t H, int64_t Dk, int64_t Dv,

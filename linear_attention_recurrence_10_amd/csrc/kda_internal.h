@@ -50,6 +50,12 @@ hipError_t launch_prefill_mfma_gate(const PrefillArgs &a, dim3 grid, hipStream_t
 bool prefill_mfma_supported(const PrefillArgs &a);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 // Segmented prefill helpers (kda_kcp.hip).
+// The fixed per-device workspace of kda_chunk_fwd_kcp_noalloc: 32 MiB, room
+// for three state sets of B * n_seg * H <= 170 heads at d = 128.
+constexpr uint64_t kKcpScratchBytes = 32ull << 20;
+constexpr int kMaxDevices = 64;
+// Its device address on the current device (looked up once per device).
+hipError_t kcp_scratch(void **ptr);
 hipError_t launch_fill_identity(float *states, int64_t n, int D, hipStream_t s);
 hipError_t launch_kcp_combine(const float *M, const float *Bs, const float *h0, float *S_in, float *hT, int64_t B,
                               int64_t P, int64_t H, int D, hipStream_t s);

@@ -9,10 +9,22 @@
 // K3 paper digest (devpress.csdn.net), section 2.4 (1), where each GPU takes a
 // segment and the states are exchanged once; here the segments are batch
 // entries of one launch and the combine is a chain of P small products.
+#include <mutex>
+
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
+
+// The segmented prefill's workspace for callers that cannot allocate
+// (kda_chunk_fwd_kcp_noalloc): one fixed array per device, held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (on the
+// host it is a stand-in symbol, not a device address); it uses the address
+// hipGetSymbolAddress returns for the current device, kept per device below.
+static __device__ __align__(256) unsigned char scratch[kKcpScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // per device ordinal; null until looked up
 
 // states[n][D][D] = I
 __global__ void fill_identity_kernel(float *states, int64_t n, int D) {
@@ -131,6 +143,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *M, const floa
 }
 
 }  // namespace
+
+hipError_t kcp_scratch(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_fill_identity(float *states, int64_t n, int D, hipStream_t s) {
     const int64_t total = n * D * D;
