@@ -32,21 +32,22 @@ import threading
 
 import numpy as np
 
-from .ref_numpy import kda_fwd_numpy  # noqa: F401  (re-export)
+from .ref_numpy import kda_bwd_numpy, kda_fwd_numpy  # noqa: F401  (re-export)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
+_SRC_BWD = os.path.join(_HERE, "kda_oracle_bwd.c")
 _LIB = os.path.join(_HERE, "libkda_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile ``kda_oracle.c`` with gcc into ``libkda_oracle.so`` (fp64, OpenMP)."""
+    """Compile ``kda_oracle.c`` and ``kda_oracle_bwd.c`` with gcc into ``libkda_oracle.so`` (fp64, OpenMP)."""
     if not force and os.path.exists(_LIB):
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", _SRC, "-o", tmp, "-lm"]
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", _SRC, _SRC_BWD, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB
@@ -63,6 +64,8 @@ def _load():
             L = ctypes.c_long
             lib.kda_oracle_fwd.argtypes = [dp] * 7 + [L] * 5 + [ctypes.c_double]
             lib.kda_oracle_fwd.restype = ctypes.c_int
+            lib.kda_oracle_bwd.argtypes = [dp] * 14 + [L] * 5 + [ctypes.c_double]
+            lib.kda_oracle_bwd.restype = ctypes.c_int
             lib.kda_oracle_num_threads.argtypes = []
             lib.kda_oracle_num_threads.restype = ctypes.c_int
             _lib = lib
@@ -120,6 +123,40 @@ def kda_fwd(q, k, v, g, beta, h0=None, scale=None):
     if rc != 0:
         raise RuntimeError("kda_oracle_fwd failed with code %d" % rc)
     return o, S
+
+
+def kda_bwd(q, k, v, g, beta, dO, h0=None, dhT=None, scale=None):
+    """Gradients of the token-sequential KDA forward pass in fp64 (C implementation).
+
+    Inputs as in :func:`kda_fwd`; dO [B, T, H, Dv] is dL/do and dhT
+    [B, H, Dk, Dv] (or None for zero) is dL/dhT.  Returns
+    (dq, dk, dv, dg, dbeta, dh0) shaped like (q, k, v, g, beta, states), fp64:
+    the plain reverse-mode adjoint of the recurrence, token by token
+    (kda_oracle_bwd.c).
+    """
+    q, k, v, g, beta, dO = (_f64(x) for x in (q, k, v, g, beta, dO))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == (B, T, H, Dk) and g.shape == (B, T, H, Dk)
+    assert v.shape == (B, T, H, Dv) and beta.shape == (B, T, H) and dO.shape == (B, T, H, Dv)
+    h0 = None if h0 is None else _f64(h0)
+    dhT = None if dhT is None else _f64(dhT)
+    for s_ in (h0, dhT):
+        assert s_ is None or s_.shape == (B, H, Dk, Dv)
+    dq, dk, dg = (np.zeros((B, T, H, Dk)) for _ in range(3))
+    dv = np.zeros((B, T, H, Dv))
+    dbeta = np.zeros((B, T, H))
+    dh0 = np.zeros((B, H, Dk, Dv))
+    if scale is None:
+        scale = Dk ** -0.5
+    null = ctypes.POINTER(ctypes.c_double)()
+    rc = _load().kda_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                null if h0 is None else _ptr(h0), _ptr(dO), null if dhT is None else _ptr(dhT),
+                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0),
+                                B, T, H, Dk, Dv, float(scale))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_bwd failed with code %d" % rc)
+    return dq, dk, dv, dg, dbeta, dh0
 
 
 def kda_decode(q, k, v, g, beta, state, scale=None):
