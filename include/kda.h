@@ -218,6 +218,54 @@ kda_status kda_chunk_fwd_kcp_noalloc(const void *q, const void *k, const void *v
 uint64_t kda_chunk_fwd_kcp_noalloc_max_bytes(void);
 
 /*
+ * kda_chunk_bwd -- gradients of kda_chunk_fwd (training; the FlashKDA kernel
+ * of the Kimi K3 paper digest, devpress.csdn.net, section 2.4 (1), serves
+ * training as well as prefill).  For a loss L with dO = dL/do and
+ * dhT = dL/dhT, it returns dL/d of every input: the reverse-mode adjoint of
+ * the recurrence at the top of this file, run from the last token to the
+ * first (with S'_t = Diag(exp g_t) S_{t-1}, r_t = S'_t^T k_t and
+ * e_t = beta_t (v_t - r_t); dS is dL/dS_t):
+ *
+ *   dS += scale q_t do_t^T        dq_t = scale S_t do_t
+ *   de  = dS^T k_t                dk_t = dS e_t + S'_t dr,   dr = -beta_t de
+ *   dbeta_t = de . (v_t - r_t)    dv_t = beta_t de
+ *   dg_t = rowsum((dS + k_t dr^T) .* S'_t)
+ *   dS  = Diag(exp g_t) (dS + k_t dr^T)          dh0 = dS after token 0
+ *
+ *   q, k, v, g, beta, h0   as for kda_chunk_fwd (h0 NULL = zeros)
+ *   dO     [B, T, H, Dv] fp32   upstream gradient of o
+ *   dhT    [B, H, Dk, Dv] fp32  upstream gradient of the final state, or NULL (zero)
+ *   dq, dk, dg [B, T, H, Dk] fp32, dv [B, T, H, Dv] fp32, dbeta [B, T, H] fp32: written
+ *   dh0    [B, H, Dk, Dv] fp32, written, or NULL (not wanted)
+ *   ws     device workspace of at least kda_chunk_bwd_ws_bytes(...) bytes,
+ *          16-byte aligned, owned by the caller, overwritten.  It holds the
+ *          forward state after every 16 tokens (written here by the prefill
+ *          kernels) and per-slice partial sums.
+ *
+ * The outputs must not overlap each other, the inputs or ws.  dq is also used
+ * as scratch for the forward pass's o before the gradient is written there.
+ * Results are deterministic (fixed summation order).  All other rules, the
+ * layouts and the errors are those of kda_chunk_fwd; T == 0 writes dh0 = dhT
+ * (or zeros).
+ */
+kda_status kda_chunk_bwd(const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, const float *h0,
+                         const float *dO, const float *dhT,
+                         float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dh0,
+                         void *ws, uint64_t ws_bytes,
+                         int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                         kda_dtype in_dtype, float scale, void *stream);
+
+/*
+ * kda_chunk_bwd_ws_bytes -- bytes of workspace kda_chunk_bwd needs:
+ * floor(T / 16) states of [B, H, Dk, Dv] fp32 plus (3 Dk + 1) B T H fp32
+ * partial sums per column slice (4 slices at Dk = 128, 1 at Dk = 16).
+ * 0 for unsupported or invalid sizes (Dk != Dv, Dk not 16 or 128, or 64-bit
+ * overflow).
+ */
+uint64_t kda_chunk_bwd_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv);
+
+/*
  * kda_decode_step -- one new token per sequence (recurrent decoding, the case
  * behind the 4x decoding speed-up at 1M tokens quoted in "Kimi K3
  * Architecture Explained", section 3): the recurrence above with T = 1,

@@ -16,7 +16,7 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_ckpt", "chunk_fwd_gate", "chunk_fwd_kcp", "chunk_fwd_kcp_noalloc", "kcp_ws_bytes", "decode_step", "KdaError", "library", "library_path", "version"]
+__all__ = ["chunk_bwd", "bwd_ws_bytes", "chunk_fwd", "chunk_fwd_ckpt", "chunk_fwd_gate", "chunk_fwd_kcp", "chunk_fwd_kcp_noalloc", "kcp_ws_bytes", "decode_step", "KdaError", "library", "library_path", "version"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -68,6 +68,11 @@ def library() -> ctypes.CDLL:
             lib.kda_chunk_fwd_kcp_noalloc_max_bytes.restype = ctypes.c_uint64
             lib.kda_chunk_fwd_kcp_ws_bytes.argtypes = [i64, i64, i64, i64, i64, i64]
             lib.kda_chunk_fwd_kcp_ws_bytes.restype = ctypes.c_uint64
+            lib.kda_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, vp,
+                                          ctypes.c_uint64, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, vp]
+            lib.kda_chunk_bwd.restype = ctypes.c_int
+            lib.kda_chunk_bwd_ws_bytes.argtypes = [i64, i64, i64, i64, i64]
+            lib.kda_chunk_bwd_ws_bytes.restype = ctypes.c_uint64
             lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, i64, i64, i64, i64,
                                             ctypes.c_int, ctypes.c_float, vp]
             lib.kda_decode_step.restype = ctypes.c_int
@@ -316,6 +321,61 @@ def chunk_fwd_ckpt(q, k, v, g, beta, h0=None, *, ckpt_every: int, scale: float |
                                   ck, int(ckpt_every), B, T, H, Dk, Dv, _dtype_code(q), float(scale or 0.0),
                                   _stream(stream)))
     return o, hT, ckpt
+
+
+def bwd_ws_bytes(B: int, T: int, H: int, Dk: int, Dv: int) -> int:
+    """Workspace bytes of :func:`chunk_bwd` (``kda_chunk_bwd_ws_bytes``)."""
+    return int(library().kda_chunk_bwd_ws_bytes(B, T, H, Dk, Dv))
+
+
+def chunk_bwd(q, k, v, g, beta, dO, h0=None, dhT=None, *, scale: float | None = None, need_dh0: bool = True,
+              ws=None, out=None, stream=None):
+    """Gradients of :func:`chunk_fwd` (``kda_chunk_bwd``).
+
+    Inputs as in :func:`chunk_fwd`; dO [B, T, H, Dv] fp32 is dL/do and dhT
+    [B, H, Dk, Dv] fp32 (or None for zero) is dL/dhT.  Returns
+    (dq, dk, dv, dg, dbeta, dh0), fp32, shaped like (q, k, v, g, beta, h0);
+    dh0 is None unless ``need_dh0``.  ``ws`` is an optional device byte
+    tensor of at least :func:`bwd_ws_bytes` bytes (allocated here when
+    omitted); ``out`` an optional tuple of the six output tensors.
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32)
+    _need(dO, "dO", torch.float32)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    for t, n in ((h0, "h0"), (dhT, "dhT")):
+        if t is not None:
+            _need(t, n, torch.float32)
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=q.device)
+        out = (torch.empty((B, T, H, Dk), **f32), torch.empty((B, T, H, Dk), **f32),
+               torch.empty((B, T, H, Dv), **f32), torch.empty((B, T, H, Dk), **f32),
+               torch.empty((B, T, H), **f32), torch.empty((B, H, Dk, Dv), **f32) if need_dh0 else None)
+    dq, dk, dv, dg, dbeta, dh0 = out
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"), (dg, "dg"), (dbeta, "dbeta")):
+        _need(t, n, torch.float32)
+    if dh0 is not None:
+        _need(dh0, "dh0", torch.float32)
+    shapes_ok = (k.shape == q.shape and g.shape == q.shape and v.shape[:3] == (B, T, H)
+                 and beta.shape == (B, T, H) and dO.shape == (B, T, H, Dv)
+                 and all(t is None or t.shape == (B, H, Dk, Dv) for t in (h0, dhT, dh0))
+                 and dq.shape == q.shape and dk.shape == q.shape and dg.shape == q.shape
+                 and dv.shape == v.shape and dbeta.shape == beta.shape)
+    if not shapes_ok:
+        raise ValueError("inconsistent shapes")
+    lib = library()
+    need = int(lib.kda_chunk_bwd_ws_bytes(B, T, H, Dk, Dv))
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(ws, "ws")
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(dO), _ptr(dhT),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(ws), ws_bytes,
+                             B, T, H, Dk, Dv, _dtype_code(q), float(scale or 0.0), _stream(stream)))
+    return dq, dk, dv, dg, dbeta, dh0
 
 
 def decode_step(q, k, v, g, beta, state, *, scale: float | None = None, o=None, stream=None):

@@ -139,7 +139,7 @@ kda_status launch_prefill(const kda::PrefillArgs &a, hipStream_t s) {
 kda_status chunk_fwd(const void *q, const void *k, const void *v, const void *g, kda::GateMode gate, float g_min,
                      const float *beta, const float *h0, float *o, float *hT, float *ckpt, int64_t ckpt_every,
                      int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale,
-                     void *stream, kda::PrefillArgs *out = nullptr) {
+                     void *stream, kda::PrefillArgs *out = nullptr, bool device_checks = true) {
     if (B <= 0 || H <= 0 || Dk <= 0 || Dv <= 0 || T < 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "sizes must be positive (T >= 0): B=%lld T=%lld H=%lld Dk=%lld Dv=%lld",
                     (long long)B, (long long)T, (long long)H, (long long)Dk, (long long)Dv);
@@ -188,10 +188,12 @@ kda_status chunk_fwd(const void *q, const void *k, const void *v, const void *g,
     for (int i = 0; i < 8; ++i) {
         if (overlaps(sp[kCk], sp[i])) return fail(KDA_ERR_INVALID_ARGUMENT, "ckpt overlaps %s", sp[i].name);
     }
-    kda_status st = check_device();
-    if (st != KDA_OK) return st;
-    st = check_spans(sp, 9);
-    if (st != KDA_OK) return st;
+    if (device_checks) {
+        kda_status st = check_device();
+        if (st != KDA_OK) return st;
+        st = check_spans(sp, 9);
+        if (st != KDA_OK) return st;
+    }
 
     kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.hT = hT;
@@ -368,6 +370,86 @@ kda_status kda_chunk_fwd_kcp_noalloc(const void *q, const void *k, const void *v
 }
 
 uint64_t kda_chunk_fwd_kcp_noalloc_max_bytes(void) { return kda::kKcpScratchBytes; }
+
+uint64_t kda_chunk_bwd_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv) {
+    if (B <= 0 || T < 0 || H <= 0 || Dk != Dv || (Dk != 16 && Dk != 128)) return 0;
+    const int64_t ns = Dk == 128 ? 4 : 1;  // column slices of the backward kernel
+    uint64_t ck = 1, pt = 1, tok = 1;
+    if (!mul_ok(ck, T / kda::kChunk) || !mul_ok(ck, B) || !mul_ok(ck, H) || !mul_ok(ck, Dk) || !mul_ok(ck, Dv))
+        return 0;
+    if (!mul_ok(tok, B) || !mul_ok(tok, T) || !mul_ok(tok, H)) return 0;
+    pt = tok;
+    if (!mul_ok(pt, 3 * Dk + 1) || !mul_ok(pt, ns)) return 0;
+    if (ck > UINT64_MAX / 8 || pt > UINT64_MAX / 8 || ck + pt > UINT64_MAX / 4) return 0;
+    const uint64_t n = ck + pt;
+    return n == 0 ? 16 : n * 4;
+}
+
+kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                         const float *h0, const float *dO, const float *dhT, float *dq, float *dk, float *dv,
+                         float *dg, float *dbeta, float *dh0, void *ws, uint64_t ws_bytes, int64_t B, int64_t T,
+                         int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale, void *stream) {
+    // the forward arguments are checked as for the prefill (with dq standing in for o: the
+    // checkpoint pass writes its o there, and the gradient overwrites it at the end)
+    // (every host-side check comes before the device is queried)
+    kda::PrefillArgs fa;
+    kda_status st = chunk_fwd(q, k, v, g, kda::kGateLogDecay, 0.f, beta, h0, dq, nullptr, nullptr, 0, B, T, H, Dk, Dv,
+                              in_dtype, scale, stream, &fa, false);
+    if (st != KDA_OK) return st;
+    if (T > 0 && (!dO || !dq || !dk || !dv || !dg || !dbeta))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "dO, dq, dk, dv, dg and dbeta must be non-null when T > 0");
+    const uint64_t need = kda_chunk_bwd_ws_bytes(B, T, H, Dk, Dv);
+    if (need == 0) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace size overflows 64 bits");
+    if (!ws || ws_bytes < need)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "ws (%llu bytes) must hold %llu bytes", (unsigned long long)ws_bytes,
+                    (unsigned long long)need);
+    const uint64_t esz = in_dtype == KDA_BF16 ? 2 : 4;
+    const uint64_t n_tok = static_cast<uint64_t>(B) * T * H, n_state = static_cast<uint64_t>(B) * H * Dk * Dv;
+    const Span sp[] = {
+        {"q", q, n_tok * Dk * esz}, {"k", k, n_tok * Dk * esz}, {"v", v, n_tok * Dv * esz},
+        {"g", g, n_tok * Dk * 4},   {"beta", beta, n_tok * 4},  {"h0", h0, n_state * 4},
+        {"dO", dO, n_tok * Dv * 4}, {"dhT", dhT, n_state * 4},  // inputs: 0 .. 7
+        {"dq", dq, n_tok * Dk * 4}, {"dk", dk, n_tok * Dk * 4}, {"dv", dv, n_tok * Dv * 4},
+        {"dg", dg, n_tok * Dk * 4}, {"dbeta", dbeta, n_tok * 4}, {"dh0", dh0, n_state * 4},
+        {"ws", ws, need},  // outputs and workspace: 8 .. 14
+    };
+    constexpr int kN = 15, kFirstOut = 8;
+    for (int i = kFirstOut; i < kN; ++i) {
+        for (int j = 0; j < kN; ++j) {
+            if (j != i && overlaps(sp[i], sp[j]))
+                return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps %s", sp[i].name, sp[j].name);
+        }
+    }
+    st = check_device();
+    if (st != KDA_OK) return st;
+    st = check_spans(sp, kN);
+    if (st != KDA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *ckpt = static_cast<float *>(ws);
+    const int64_t n_ck = T / kda::kChunk;
+    // the states after every 16 tokens (o goes to dq, overwritten below)
+    if (n_ck > 0) {
+        kda::PrefillArgs ca = fa;
+        ca.o = dq;
+        ca.hT = nullptr;
+        ca.ckpt = ckpt;
+        ca.ckpt_every = 1;
+        ca.n_ckpt = n_ck;
+        st = launch_prefill(ca, s);
+        if (st != KDA_OK) return st;
+    }
+    kda::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.dO = dO; a.dhT = dhT; a.ckpt = ckpt;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+    a.part = ckpt + static_cast<uint64_t>(n_ck) * n_state;
+    a.part_plane = static_cast<int64_t>(n_tok * Dk);
+    a.part_stride = static_cast<int64_t>(n_tok * (3 * Dk + 1));
+    a.B = B; a.T = T; a.H = H; a.D = static_cast<int>(Dk);
+    a.bf16 = in_dtype == KDA_BF16;
+    a.scale = fa.scale;
+    if (T == 0 && !dh0) return ok();
+    return launch_status(kda::launch_bwd(a, s), "kda backward");
+}
 
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
                            float *state, float *o, int64_t B, int64_t H, int64_t Dk, int64_t Dv,

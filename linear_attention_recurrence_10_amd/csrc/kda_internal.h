@@ -43,7 +43,27 @@ struct DecodeArgs {
     float scale;
 };
 
+// The backward pass (kda_bwd.hip): gradients of every input given dO and dhT.
+struct BwdArgs {
+    const void *q, *k, *v;   // [B,T,H,D] in dtype
+    const float *g, *beta;   // [B,T,H,D], [B,T,H]
+    const float *h0;         // [B,H,D,D] or null
+    const float *dO;         // [B,T,H,D]
+    const float *dhT;        // [B,H,D,D] or null (zero)
+    const float *ckpt;       // [T / 16, B,H,D,D]: the state after every 16 tokens
+    float *dq, *dk, *dv, *dg, *dbeta;  // like q, k, v, g, beta
+    float *dh0;              // [B,H,D,D] or null
+    float *part;             // per-slice sums over columns: [slices][3 planes of B T H D, then B T H]
+    int64_t part_stride;     // floats per slice
+    int64_t part_plane;      // B T H D
+    int64_t B, T, H;
+    int D;
+    bool bf16;
+    float scale;
+};
+
 // Each launcher returns hipSuccess or the launch error; all are asynchronous.
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_mfma_gate(const PrefillArgs &a, dim3 grid, hipStream_t s);  // gate-logit variants

@@ -215,3 +215,51 @@ def test_kcp_workspace_checks(lib):
 def test_kcp_shares_the_prefill_checks(lib):
     assert chunk_kcp(lib, n_seg=1, D=64) == 2          # one segment is the plain prefill
     assert chunk_kcp(lib, B=0) == 1 and b"sizes" in lib.kda_last_error()
+
+
+# --- the backward pass (host-side validation only) ------------------------
+
+def distinct(n=15):
+    """Fake, non-overlapping, aligned addresses (never dereferenced)."""
+    return [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(n)]
+
+
+def bwd(lib, B=1, T=16, H=1, Dk=128, Dv=128, ws_bytes=1 << 30, ptrs=None):
+    p = ptrs or distinct()
+    return lib.kda_chunk_bwd(*p[:15], ws_bytes, B, T, H, Dk, Dv, 1, 0.0, None)
+
+
+def test_bwd_workspace_size(lib):
+    # floor(T / 16) states plus (3 D + 1) B T H partials per slice (4 slices at D = 128)
+    assert lib.kda_chunk_bwd_ws_bytes(1, 64, 2, 128, 128) == 4 * (4 * 2 * 128 * 128 + 4 * 64 * 2 * (3 * 128 + 1))
+    assert lib.kda_chunk_bwd_ws_bytes(2, 17, 3, 16, 16) == 4 * (1 * 6 * 16 * 16 + 1 * 2 * 17 * 3 * (3 * 16 + 1))
+    assert lib.kda_chunk_bwd_ws_bytes(1, 16, 1, 128, 64) == 0
+    assert lib.kda_chunk_bwd_ws_bytes(1, 16, 1, 64, 64) == 0
+    assert lib.kda_chunk_bwd_ws_bytes(0, 16, 1, 128, 128) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(T=-1), dict(H=0), dict(Dk=64, Dv=64), dict(Dk=128, Dv=16)])
+def test_bwd_rejects_bad_sizes(lib, kw):
+    assert bwd(lib, **kw) in (1, 2)
+
+
+def test_bwd_null_gradient_outputs(lib):
+    p = distinct()
+    p[8] = None  # dq
+    assert bwd(lib, ptrs=p) == 1
+    p = distinct()
+    p[6] = None  # dO
+    assert bwd(lib, ptrs=p) == 1
+
+
+def test_bwd_small_workspace(lib):
+    need = lib.kda_chunk_bwd_ws_bytes(1, 16, 1, 128, 128)
+    assert bwd(lib, ws_bytes=need - 1) == 1
+    assert b"ws" in lib.kda_last_error()
+
+
+def test_bwd_outputs_must_not_overlap(lib):
+    p = distinct()
+    p[9] = p[8]  # dk == dq
+    assert bwd(lib, ptrs=p) == 1
+    assert b"overlaps" in lib.kda_last_error()

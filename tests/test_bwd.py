@@ -1,0 +1,154 @@
+"""The backward pass (kda_chunk_bwd) against the fp64 backward oracle.
+
+Gradients of L = sum(o * dO) + sum(hT * dhT) with respect to q, k, v, g,
+beta and h0, element by element through the C ABI.  Tolerance per gradient
+tensor: max|gpu - oracle| / rms(oracle) <= 2e-2 for bf16 q/k/v and <= 1e-4
+for fp32 q/k/v (the bars of the forward pass; the backward adds fp32
+arithmetic on top of the forward's checkpointed states).
+"""
+from __future__ import annotations
+
+import sys
+
+import pytest
+import torch
+
+import kda_inputs
+import linear_attention_recurrence_10_amd as kda
+import oracle
+from gpu_helpers import ErrAcc, head_groups, host64, rel_err, tol_for
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def upstream(B, T, H, D, seed, dhT=True):
+    gen = torch.Generator(device=DEV).manual_seed(seed)
+    dO = torch.randn((B, T, H, D), generator=gen, device=DEV)
+    dh = torch.randn((B, H, D, D), generator=gen, device=DEV) if dhT else None
+    return dO, dh
+
+
+def run(x, dO, dhT, need_dh0=True):
+    out = kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dO, x.get("h0"), dhT, need_dh0=need_dh0)
+    torch.cuda.synchronize()
+    return out
+
+
+def reference(x, dO, dhT):
+    args = [host64(x[n]) for n in ("q", "k", "v", "g", "beta")]
+    h0 = x.get("h0")
+    return oracle.kda_bwd(*args, host64(dO), h0=None if h0 is None else host64(h0),
+                          dhT=None if dhT is None else host64(dhT))
+
+
+def check(x, dO, dhT, dtype, label, need_dh0=True):
+    got = run(x, dO, dhT, need_dh0)
+    ref = reference(x, dO, dhT)
+    errs = {}
+    for n, gv, rv in zip(NAMES, got, ref):
+        if gv is None:
+            continue
+        errs[n] = rel_err(gv.cpu(), rv)
+    say("%s: %s" % (label, " ".join("%s=%.2e" % kv for kv in errs.items())))
+    tol = tol_for(dtype)
+    for n, e in errs.items():
+        assert e <= tol, (label, n, e)
+    return errs
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [16, 128])
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 50, 130])
+def test_bwd_parity(dtype, D, T):
+    x = kda_inputs.prefill_inputs(2, T, 3, D, dtype, h0=True, seed=500 + T + D, device=DEV)
+    dO, dhT = upstream(2, T, 3, D, seed=T + D)
+    check(x, dO, dhT, dtype, "bwd %s D=%d T=%d" % (dtype, D, T))
+
+
+def test_bwd_tiny_f32_d16():
+    cfg = kda_inputs.TINY
+    x = kda_inputs.config_inputs(cfg, device=DEV)
+    dO, dhT = upstream(cfg.B, cfg.T, cfg.H, cfg.D, seed=1)
+    check(x, dO, dhT, cfg.dtype, "bwd " + cfg.name)
+
+
+def test_bwd_b4_h16_t4096_whole():
+    """The B=4, H=16, T=4096 workload with random h0 and dhT, every element
+    of every gradient against the oracle (16 heads at a time)."""
+    cfg = kda_inputs.PREFILL_B4
+    say("case bwd " + cfg.name)
+    x = kda_inputs.config_inputs(cfg, device=DEV)
+    dO, dhT = upstream(cfg.B, cfg.T, cfg.H, cfg.D, seed=2)
+    got = run(x, dO, dhT)
+    accs = {n: ErrAcc() for n in NAMES}
+    for heads in head_groups(cfg.H, 8):
+        hi = torch.as_tensor(heads, device=DEV)
+        sub = {n: x[n].index_select(2, hi) for n in ("q", "k", "v", "g", "beta")}
+        sub["h0"] = x["h0"].index_select(1, hi)
+        ref = reference(sub, dO.index_select(2, hi), dhT.index_select(1, hi))
+        for n, gv, rv in zip(NAMES, got, ref):
+            dim = 1 if n == "dh0" else 2
+            accs[n].add(gv.index_select(dim, hi), rv)
+    errs = {n: a.value() for n, a in accs.items()}
+    say("bwd %s whole tensors: %s" % (cfg.name, " ".join("%s=%.2e" % kv for kv in errs.items())))
+    for n, e in errs.items():
+        assert e <= 2e-2, (n, e)
+
+
+@pytest.mark.parametrize("kind", ["floor_gate", "no_decay", "beta_one", "beta_zero", "weak_decay"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_stress(kind, dtype):
+    x = kda_inputs.prefill_inputs(1, 96, 2, 128, dtype, h0=True, seed=31, device=DEV,
+                                  gate_mean=(-4.0 if kind == "weak_decay" else 0.0))
+    if kind == "floor_gate":
+        x["g"].fill_(-5.0)
+    elif kind == "no_decay":
+        x["g"].zero_()
+    elif kind == "beta_one":
+        x["beta"].fill_(1.0)
+    elif kind == "beta_zero":
+        x["beta"].zero_()
+    dO, dhT = upstream(1, 96, 2, 128, seed=3)
+    check(x, dO, dhT, dtype, "bwd stress %s %s" % (kind, dtype))
+
+
+def test_bwd_without_initial_state_or_final_gradient():
+    x = kda_inputs.prefill_inputs(2, 70, 2, 128, "bf16", h0=False, seed=33, device=DEV)
+    dO, _ = upstream(2, 70, 2, 128, seed=4, dhT=False)
+    check(x, dO, None, "bf16", "bwd no h0 no dhT")
+    out = run(x, dO, None, need_dh0=False)
+    assert out[5] is None
+
+
+def test_bwd_empty_sequence():
+    x = kda_inputs.prefill_inputs(2, 0, 3, 128, "bf16", h0=True, seed=34, device=DEV)
+    dO, dhT = upstream(2, 0, 3, 128, seed=5)
+    out = run(x, dO, dhT)
+    assert out[0].shape == (2, 0, 3, 128)
+    assert torch.equal(out[5], dhT)
+
+
+def test_bwd_repeat_runs_are_bitwise_identical():
+    """The per-slice sums over columns are added in a fixed order."""
+    x = kda_inputs.prefill_inputs(2, 200, 4, 128, "bf16", h0=True, seed=35, device=DEV)
+    dO, dhT = upstream(2, 200, 4, 128, seed=6)
+    a = run(x, dO, dhT)
+    b = run(x, dO, dhT)
+    for n, u, w in zip(NAMES, a, b):
+        assert torch.equal(u, w), n
+
+
+def test_bwd_rejects_a_small_workspace():
+    x = kda_inputs.prefill_inputs(1, 32, 1, 128, "bf16", seed=36, device=DEV)
+    dO, _ = upstream(1, 32, 1, 128, seed=7, dhT=False)
+    need = kda.bwd_ws_bytes(1, 32, 1, 128, 128)
+    ws = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(kda.KdaError):
+        kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dO, ws=ws)
