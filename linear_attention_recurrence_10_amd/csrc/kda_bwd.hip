@@ -316,6 +316,210 @@ __global__ __launch_bounds__(64 * BwdShape<D>::kNW) void bwd_kernel(BwdArgs a) {
     }
 }
 
+// The adjoint at Dk = Dv = 128 with a column per wave: work-group (b, h,
+// slice) of 8 waves, wave w owns the slice's columns 4 w .. 4 w + 3 over all
+// 128 rows, lane l rows 2 l and 2 l + 1.  A sum over the rows of a column
+// (r_t, de) then stays inside one wave: a sum over each 16-lane row by DPP and
+// four lane reads, the same value in every lane, with no barrier.  The
+// forward steps that re-form the states of a block need only those sums, so
+// all 16 states of a block are formed at once and kept in registers.  Sums
+// over the columns of a row (dq, dk, dg) and over the columns (dbeta) are
+// outputs that nothing waits for: each wave leaves its share of 8 tokens in
+// LDS and they are summed over the waves once per 8 tokens.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mv(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// the sum of x over all 64 lanes, in every lane (a fixed order: deterministic)
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_mv<0xb1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+    x += dpp_mv<0x4e>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    x += dpp_mv<0x141>(x);  // row_half_mirror: the other quad of the 8
+    x += dpp_mv<0x140>(x);  // row_mirror: the other 8 of the 16-lane row
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(512) void bwd_col_kernel(BwdArgs a) {
+    constexpr int D = 128, kCW = 32, kNW = 8, kCPW = kCW / kNW;  // 4 columns per wave
+    constexpr int kRPL = 2;                                      // rows per lane
+    constexpr int kNS = D / kCW;
+    constexpr int kNQ = 3;  // sums over a row's columns: dq, dk, dg
+    __shared__ float rowp[kHalf][kNQ][kNW][D];  // each wave's sums over its columns, 8 tokens
+    __shared__ float dbp[kHalf][kNW];           // each wave's share of dbeta, 8 tokens
+    __shared__ float keep_e[kBlk][kCW];         // e_t of the block, by column
+    __shared__ float keep_r[kBlk][kCW];         // r_t of the block
+    __shared__ float s_k[kBlk][D], s_q[kBlk][D], s_a[kBlk][D];
+    __shared__ float s_v[kBlk][kCW], s_do[kBlk][kCW];
+    __shared__ float s_b[kBlk];
+
+    const int64_t bh = blockIdx.x / kNS;
+    const int slice = static_cast<int>(blockIdx.x % kNS);
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int r0 = kRPL * lane;                 // first row of this lane
+    const int c0 = kCPW * w;                    // first column of this wave within the slice
+    const int col0 = slice * kCW + c0;
+    const int64_t T = a.T, H = a.H;
+    const int64_t sbase = bh * D * D + static_cast<int64_t>(r0) * D + col0;
+    float *part = a.part + static_cast<int64_t>(slice) * a.part_stride;
+
+    float dS[kRPL][kCPW];
+#pragma unroll
+    for (int i = 0; i < kRPL; ++i)
+#pragma unroll
+        for (int j = 0; j < kCPW; ++j) dS[i][j] = a.dhT ? a.dhT[sbase + i * D + j] : 0.f;
+
+    const int64_t nblk = (T + kBlk - 1) / kBlk;
+    const int64_t BHD = a.B * a.H * D * D;
+    for (int64_t m = nblk - 1; m >= 0; --m) {
+        const int64_t t0 = m * kBlk;
+        const int nt = static_cast<int>((t0 + kBlk < T ? t0 + kBlk : T) - t0);
+        __syncthreads();  // the previous block is done with the staged inputs
+        for (int idx = tid; idx < kBlk * D; idx += 512) {
+            const int u = idx / D, c = idx % D;
+            if (u < nt) {
+                const int64_t o = ((b * T + t0 + u) * H + h) * D + c;
+                s_k[u][c] = ld_in(a.k, o, BF16);
+                s_q[u][c] = ld_in(a.q, o, BF16);
+                s_a[u][c] = __expf(a.g[o]);
+            }
+        }
+        for (int idx = tid; idx < kBlk * kCW; idx += 512) {
+            const int u = idx / kCW, c = idx % kCW;
+            if (u < nt) {
+                const int64_t o = ((b * T + t0 + u) * H + h) * D + slice * kCW + c;
+                s_v[u][c] = ld_in(a.v, o, BF16);
+                s_do[u][c] = a.dO[o];
+            }
+        }
+        if (tid < nt) s_b[tid] = a.beta[(b * T + t0 + tid) * H + h];
+        __syncthreads();
+        // the states before each token of the block, formed from the checkpoint
+        float S[kRPL][kCPW];
+#pragma unroll
+        for (int i = 0; i < kRPL; ++i)
+#pragma unroll
+            for (int j = 0; j < kCPW; ++j)
+                S[i][j] = m == 0 ? (a.h0 ? a.h0[sbase + i * D + j] : 0.f) : a.ckpt[(m - 1) * BHD + sbase + i * D + j];
+        float st[kBlk][kRPL][kCPW];
+#pragma unroll
+        for (int u = 0; u < kBlk; ++u) {
+            if (u < nt) {
+                float kk[kRPL], ai[kRPL];
+#pragma unroll
+                for (int i = 0; i < kRPL; ++i) {
+                    kk[i] = s_k[u][r0 + i];
+                    ai[i] = s_a[u][r0 + i];
+                }
+                const float bt = s_b[u];
+#pragma unroll
+                for (int j = 0; j < kCPW; ++j) {
+                    float pr = 0.f;
+#pragma unroll
+                    for (int i = 0; i < kRPL; ++i) {
+                        st[u][i][j] = S[i][j];
+                        S[i][j] *= ai[i];  // S'_t
+                        pr += S[i][j] * kk[i];
+                    }
+                    const float r = wave_sum(pr);
+                    const float e = bt * (s_v[u][c0 + j] - r);
+#pragma unroll
+                    for (int i = 0; i < kRPL; ++i) S[i][j] += kk[i] * e;
+                    if (lane == 0) {
+                        keep_e[u][c0 + j] = e;
+                        keep_r[u][c0 + j] = r;
+                    }
+                }
+            }
+        }
+        // (each wave reads only its own columns of keep_e / keep_r: no barrier needed)
+        // the adjoint over the block, last token first; the sums over the
+        // waves are taken after every 8 tokens
+#pragma unroll
+        for (int u = kBlk - 1; u >= 0; --u) {
+            if (u >= nt) continue;
+            const int64_t rt = (b * T + t0 + u) * H + h;
+            const int us = u & (kHalf - 1);  // slot of the token in rowp / dbp
+            float kk[kRPL], qq[kRPL], ai[kRPL];
+#pragma unroll
+            for (int i = 0; i < kRPL; ++i) {
+                kk[i] = s_k[u][r0 + i];
+                qq[i] = s_q[u][r0 + i];
+                ai[i] = s_a[u][r0 + i];
+            }
+            const float bt = s_b[u];
+            float sq[kRPL] = {}, se[kRPL] = {}, sdr[kRPL] = {}, sg[kRPL] = {};
+            float dbw = 0.f;
+#pragma unroll
+            for (int j = 0; j < kCPW; ++j) {
+                const float e = keep_e[u][c0 + j], rr = keep_r[u][c0 + j];
+                const float dov = s_do[u][c0 + j], vv = s_v[u][c0 + j];
+                float sp[kRPL], pk = 0.f;
+#pragma unroll
+                for (int i = 0; i < kRPL; ++i) {
+                    sp[i] = ai[i] * st[u][i][j];
+                    dS[i][j] += a.scale * qq[i] * dov;          // o_t = scale S_t^T q_t
+                    sq[i] += (sp[i] + kk[i] * e) * dov;
+                    pk += dS[i][j] * kk[i];                     // S_t = S'_t + k_t e_t^T
+                    se[i] += dS[i][j] * e;
+                }
+                const float de = wave_sum(pk);
+                dbw += de * (vv - rr);                          // e_t = beta_t (v_t - r_t)
+                const float dr = -bt * de;
+#pragma unroll
+                for (int i = 0; i < kRPL; ++i) {
+                    const float dsp = dS[i][j] + kk[i] * dr;    // r_t = S'_t^T k_t
+                    sdr[i] += sp[i] * dr;
+                    sg[i] += dsp * sp[i];                       // S'_t = Diag(exp g_t) S_{t-1}
+                    dS[i][j] = ai[i] * dsp;
+                }
+                if (lane == 0) a.dv[rt * D + col0 + j] = bt * de;
+            }
+            // this wave's sums over its columns, to be summed over the waves
+#pragma unroll
+            for (int i = 0; i < kRPL; ++i) {
+                rowp[us][0][w][r0 + i] = a.scale * sq[i];
+                rowp[us][1][w][r0 + i] = se[i] + sdr[i];
+                rowp[us][2][w][r0 + i] = sg[i];
+            }
+            if (lane == 0) dbp[us][w] = dbw;
+            if (us == 0) {
+                // tokens u .. min(u + 8, nt) - 1 of the block are done by every wave
+                __syncthreads();
+                const int n8 = nt - u < kHalf ? nt - u : kHalf;
+                const int64_t rt0 = (b * T + t0 + u) * H + h;  // token u; token u + s is H rows later
+                for (int idx = tid; idx < kNQ * D; idx += 512) {
+                    const int q = idx / D, r = idx % D;
+                    for (int s8 = 0; s8 < n8; ++s8) {
+                        float x = rowp[s8][q][0][r];
+#pragma unroll
+                        for (int ww = 1; ww < kNW; ++ww) x += rowp[s8][q][ww][r];
+                        part[q * a.part_plane + (rt0 + s8 * H) * D + r] = x;
+                    }
+                }
+                if (tid < n8) {
+                    float x = dbp[tid][0];
+#pragma unroll
+                    for (int ww = 1; ww < kNW; ++ww) x += dbp[tid][ww];
+                    part[3 * a.part_plane + rt0 + tid * H] = x;
+                }
+                __syncthreads();  // rowp / dbp are written again by the next 8 tokens
+            }
+        }
+    }
+    if (a.dh0) {
+#pragma unroll
+        for (int i = 0; i < kRPL; ++i)
+#pragma unroll
+            for (int j = 0; j < kCPW; ++j) a.dh0[sbase + i * D + j] = dS[i][j];
+    }
+}
+
 // A slice's partials are three planes of n_tok * D values (dq, dk, dg) and
 // then n_tok values (dbeta).
 __global__ void bwd_sum_kernel(const float *part, int64_t stride, int64_t plane, int ns, float *dq, float *dk,
@@ -337,8 +541,8 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
     const int64_t BH = a.B * a.H;
     if (a.D == 128) {
         const dim3 grid(static_cast<unsigned>(BH * 4));
-        if (a.bf16) hipLaunchKernelGGL((bwd_kernel<128, true>), grid, dim3(512), 0, s, a);
-        else hipLaunchKernelGGL((bwd_kernel<128, false>), grid, dim3(512), 0, s, a);
+        if (a.bf16) hipLaunchKernelGGL((bwd_col_kernel<true>), grid, dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((bwd_col_kernel<false>), grid, dim3(512), 0, s, a);
     } else if (a.D == 16) {
         const dim3 grid(static_cast<unsigned>(BH));
         if (a.bf16) hipLaunchKernelGGL((bwd_kernel<16, true>), grid, dim3(64), 0, s, a);
