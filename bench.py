@@ -13,6 +13,9 @@ Prints ONE JSON line on stdout:
   decode         the decode kernel's algorithmic GB/s against the HBM peak
   segmented      the segmented prefill (kda_chunk_fwd_kcp) beside the single
                  pass on one long sequence with 7 heads (B=1, T=262144)
+  backward       the backward pass (kda_chunk_bwd) at B=4 H=16 T=4096
+  configs        the other prefill workloads (tiny fp32, B=4 H=16 T=4096, T=2^20)
+  copy           a plain 1 GiB device copy (the streaming rate this part reaches)
   cpu_baseline   the fp64 oracle on the host cores, on a bounded token sample
 """
 from __future__ import annotations
@@ -49,6 +52,14 @@ def prefill_bytes(B, T, H, D, in_bytes=2, h0=False, hT=True, gate_bytes=4):
     per_tok_head = 3 * D * in_bytes + gate_bytes * D + 4 + 4 * D
     state = 4 * D * D
     return B * T * H * per_tok_head + B * H * state * (int(h0) + int(hT))
+
+
+def backward_bytes(B, T, H, D, in_bytes=2, h0=True, dhT=True, dh0=True):
+    """Algorithmic HBM bytes of one backward pass: q, k, v (in dtype), g, beta
+    and dO (fp32) read once; dq, dk, dg, dv, dbeta (fp32) written once; the
+    states h0 and dhT read and dh0 written once."""
+    per_tok_head = 3 * D * in_bytes + 4 * D + 4 + 4 * D + 4 * (3 * D + D) + 4
+    return B * T * H * per_tok_head + B * H * 4 * D * D * (int(h0) + int(dhT) + int(dh0))
 
 
 def decode_bytes(B, H, D, in_bytes=2):
@@ -198,6 +209,47 @@ def time_configs(kda, torch, stream, names, steps):
     return out
 
 
+def time_backward(kda, torch, stream, steps, calibrate=False):
+    """The backward pass (kda_chunk_bwd: forward checkpoints, the adjoint, the
+    slice sums) on the B=4 H=16 T=4096 workload with random dO and dhT.
+    ``calibrate``: run the plain copy of COPY_BYTES right before the first
+    backward launch (the reference of the traffic counters)."""
+    import kda_inputs
+
+    cfg = kda_inputs.PREFILL_B4
+    dev = torch.device("cuda:0")
+    log("backward: %s" % cfg.name)
+    x = kda_inputs.config_inputs(cfg, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(2)
+    dO = torch.randn((cfg.B, cfg.T, cfg.H, cfg.D), generator=gen, device=dev)
+    dhT = torch.randn((cfg.B, cfg.H, cfg.D, cfg.D), generator=gen, device=dev)
+    ws = torch.empty(kda.bwd_ws_bytes(cfg.B, cfg.T, cfg.H, cfg.D, cfg.D), dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = (torch.empty_like(dO), torch.empty_like(dO), torch.empty_like(dO), torch.empty_like(dO),
+           torch.empty((cfg.B, cfg.T, cfg.H), **f32), torch.empty((cfg.B, cfg.H, cfg.D, cfg.D), **f32))
+
+    def fn():
+        kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dO, x["h0"], dhT, ws=ws, out=out, stream=stream)
+
+    if calibrate:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    avg, mn = time_launches(torch, stream, fn, max(3, steps // 4))
+    nbytes = backward_bytes(cfg.B, cfg.T, cfg.H, cfg.D)
+    gbps = nbytes / (avg * 1e-3) / 1e9
+    del x, dO, dhT, ws, out
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "ms": avg, "min_ms": mn, "tokens_per_s": cfg.B * cfg.T / (avg * 1e-3),
+            "alg_bytes_per_launch": nbytes, "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": gbps / HBM_PEAK_GBPS,
+            "note": "forward checkpoint pass + token-serial fp32 adjoint + slice sums; vector-ALU bound"}
+
+
 def copy_bandwidth(torch, stream, nbytes=1 << 30, steps=10):
     """A plain device-to-device copy of nbytes: the streaming rate this part
     reaches (read + write bytes over time), context for the HBM fractions."""
@@ -262,8 +314,13 @@ def main():
                          "long 7-head sequence, beside the single pass (0 = skip)")
     ap.add_argument("--segmented-only", action="store_true",
                     help="time only the segmented prefill (for a kernel trace of its launches alone)")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
+    ap.add_argument("--no-host-cost", action="store_true",
+                    help="skip the host cost per decode call (its small launches would mix into a kernel trace)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip timing the other prefill workloads (tiny, B=4 H=16 T=4096, T=2^20)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward pass (for a kernel trace of its launches alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain device copy of %d bytes first (for the traffic counters)" % (1 << 30))
     args = ap.parse_args()
@@ -285,6 +342,14 @@ def main():
     kda.library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.backward_only:
+        bw = time_backward(kda, torch, torch.cuda.current_stream(), args.steps, calibrate=args.copy_calibration)
+        print(json.dumps({"metric": "KDA backward tokens/s", "value": bw["tokens_per_s"], "unit": "tokens/s",
+                          "n_gpus": 1, "steps": max(3, args.steps // 4), "warmup": 1, "ms_per_step": bw["ms"],
+                          "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+                          "config": {"workload": bw["workload"]}, "backward": bw}), flush=True)
+        return
 
     if args.segmented_only:
         n_seg = args.segments if args.segments > 0 else 8
@@ -446,7 +511,9 @@ def main():
     if seg is not None:
         result["segmented"] = seg
     result["copy"] = copy_bandwidth(torch, stream)
-    if d is not None:
+    if not args.no_backward:
+        result["backward"] = time_backward(kda, torch, stream, args.steps)
+    if d is not None and not args.no_host_cost:
         result["decode"]["host"] = decode_host_cost(kda, torch)
     if not args.no_configs:
         import kda_inputs

@@ -4,11 +4,11 @@ Inputs are three rocprofv3 output directories made with the commands below
 (each one a separate run; counters never share a run with other tracing):
 
   rocprofv3 --kernel-trace --stats --output-format csv -d DIR_T -o trace -- \\
-      python3 bench.py --steps 20 --warmup 1 --no-cpu-baseline --segments 0
+      python3 bench.py --steps 20 --warmup 1 --no-cpu-baseline --segments 0 --no-configs --no-backward --no-host-cost
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR_F -o fetch -- \\
-      python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --copy-calibration
+      python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --no-configs --no-backward --no-host-cost --copy-calibration
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR_W -o write -- \\
-      python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --copy-calibration
+      python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --no-configs --no-backward --no-host-cost --copy-calibration
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
 counter reads for the runtime's plain copy of COPY_BYTES bytes, so that a
@@ -21,6 +21,8 @@ usage: python3 bench_traffic.py DIR_T DIR_F DIR_W OUT
            bench.py --segmented-only: OUT/kda_prefill_256k_h7_segmented_rocprof.md)
        python3 bench_traffic.py --util DIR_U OUT   (issue and pipe utilisation of the
            prefill from one counter run: OUT/kda_prefill_64k_util.md)
+       python3 bench_traffic.py --backward DIR_T DIR_F DIR_W OUT   (trace and traffic of
+           bench.py --backward-only: OUT/kda_bwd_b4_h16_t4096_rocprof.md)
 """
 from __future__ import annotations
 
@@ -132,11 +134,11 @@ def main(dt, df, dw, out):
              "the fused gate prologue) and decode (B=256 H=56 d=128)", "",
              "Commands (from the repository root):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d DIR_T -o trace -- "
-             "python3 bench.py --steps 20 --warmup 1 --no-cpu-baseline --segments 0",
+             "python3 bench.py --steps 20 --warmup 1 --no-cpu-baseline --segments 0 --no-configs --no-backward --no-host-cost",
              "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR_F -o fetch -- "
-             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --copy-calibration",
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --no-configs --no-backward --no-host-cost --copy-calibration",
              "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR_W -o write -- "
-             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --copy-calibration",
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --no-configs --no-backward --no-host-cost --copy-calibration",
              "    python3 bench_traffic.py DIR_T DIR_F DIR_W profiles", "",
              "Kernel source hash: prefill %s, decode %s" % (res["kernel_src_sha"], res["decode_src_sha"]), "",
              "## Kernel trace (--stats)", "",
@@ -200,6 +202,61 @@ def segmented(dt, out, n_seg):
     print("\n".join(lines))
 
 
+BWD_KERNELS = (("prefill_mfma_kernel<true, 0, 0>", "forward with a state checkpoint every 16 tokens"),
+               ("bwd_col_kernel<true>", "token-serial adjoint, 32-column slices"),
+               ("bwd_sum_kernel", "sum of the slices' partial sums (dq, dk, dg, dbeta)"))
+
+
+def backward(dt, df, dw, out):
+    """Kernel trace and HBM traffic of ``bench.py --backward-only`` (B=4 H=16 T=4096)."""
+    stats = _csv(dt, "kernel_stats.csv")
+    fetch = per_dispatch(df, "FETCH_SIZE")
+    write = per_dispatch(dw, "WRITE_SIZE")
+
+    def calib(disp):
+        first = min(k for k, (name, _) in disp.items() if "kda::" in name)
+        copies = [k for k, (name, _) in disp.items() if COPY in name and k < first]
+        if not copies:
+            raise SystemExit("copy calibration dispatch not found")
+        return disp[max(copies)][1]
+
+    kib = bench.COPY_BYTES / 1024.0
+    sf, sw = kib / calib(fetch), kib / calib(write)
+    cmds = ["rocprofv3 --kernel-trace --stats --output-format csv -d DIR_T -o trace -- "
+            "python3 bench.py --backward-only --steps 20",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR_F -o fetch -- "
+            "python3 bench.py --backward-only --steps 4 --copy-calibration",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR_W -o write -- "
+            "python3 bench.py --backward-only --steps 4 --copy-calibration",
+            "python3 bench_traffic.py --backward DIR_T DIR_F DIR_W profiles"]
+    alg = bench.backward_bytes(4, 4096, 16, 128)
+    lines = ["# rocprofv3: KDA backward pass (B=4 H=16 T=4096 d=128, bf16 q/k/v, random h0, dO and dhT)", "",
+             "Commands (from the repository root):", ""] + ["    " + c for c in cmds] + [
+             "", "Kernel source hash: backward %s, prefill %s" % (
+                 bench.source_hash([os.path.join(bench._CSRC, "kda_bwd.hip"), os.path.join(bench._CSRC, "kda_internal.h")]),
+                 bench.source_hash()),
+             "", "Copy calibration scale factors %.4f (fetch), %.4f (write)." % (sf, sw), "",
+             "| kernel | role | calls | avg us | min us | scaled HBM bytes per launch |", "|---|---|---|---|---|---|"]
+    total_t, total_b = 0.0, 0.0
+    for key, role in BWD_KERNELS:
+        f, _ = mean_for(fetch, key)
+        w, _ = mean_for(write, key)
+        hb = (f or 0.0) * 1024 * sf + (w or 0.0) * 1024 * sw
+        for r in stats:
+            if key in r["Name"]:
+                avg = float(r["AverageNs"]) / 1e3
+                total_t += avg
+                total_b += hb
+                lines.append("| %s | %s | %d | %.1f | %.1f | %.4g |" % (key, role, int(r["Calls"]), avg,
+                                                                      float(r["MinNs"]) / 1e3, hb))
+    lines += ["", "One backward pass: %.1f us, %.4g HBM bytes (counters) against %.4g algorithmic bytes "
+              "(%.2fx)." % (total_t, total_b, alg, total_b / alg)]
+    os.makedirs(out, exist_ok=True)
+    with open(os.path.join(out, "kda_bwd_b4_h16_t4096_rocprof.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_MFMA "
                  "SQ_INSTS_SALU SQ_INSTS_LDS GRBM_GUI_ACTIVE")
 
@@ -208,7 +265,7 @@ def utilisation(du, out, cus=256, simds_per_cu=4, xcds=8):
     """Issue and pipe-busy summary of the plain prefill from one counter run:
 
     rocprofv3 --pmc <UTIL_COUNTERS> --output-format csv -d DIR_U -o util -- \
-        python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --no-decode --gate-logits none
+        python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --no-configs --no-backward --no-host-cost --no-decode --gate-logits none
     """
     import collections
     rows = _csv(du, "counter_collection.csv")
@@ -224,7 +281,7 @@ def utilisation(du, out, cus=256, simds_per_cu=4, xcds=8):
     wgs = 56 * 4
     per_chunk_simd = lambda c: m[c] / (wgs * simds_per_cu * steps)
     cmd = ("rocprofv3 --pmc %s --output-format csv -d DIR_U -o util -- python3 bench.py --steps 2 --warmup 1 "
-           "--no-cpu-baseline --segments 0 --no-decode --gate-logits none" % UTIL_COUNTERS)
+           "--no-cpu-baseline --segments 0 --no-configs --no-backward --no-host-cost --no-decode --gate-logits none" % UTIL_COUNTERS)
     lines = ["# rocprofv3: KDA prefill (B=1 H=56 T=65536 d=128) issue and pipe utilisation", "",
              "Commands (from the repository root):", "", "    " + cmd,
              "    python3 bench_traffic.py --util DIR_U profiles", "",
@@ -251,6 +308,9 @@ def utilisation(du, out, cus=256, simds_per_cu=4, xcds=8):
 if __name__ == "__main__":
     if len(sys.argv) == 4 and sys.argv[1] == "--util":
         utilisation(sys.argv[2], sys.argv[3])
+        sys.exit(0)
+    if len(sys.argv) == 6 and sys.argv[1] == "--backward":
+        backward(*sys.argv[2:])
         sys.exit(0)
     if len(sys.argv) == 5 and sys.argv[1] == "--segmented":
         segmented(sys.argv[3], sys.argv[4], int(sys.argv[2]))
