@@ -152,3 +152,35 @@ def test_bwd_rejects_a_small_workspace():
     ws = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
     with pytest.raises(kda.KdaError):
         kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dO, ws=ws)
+
+
+@pytest.mark.parametrize("T1", [16, 45])
+def test_bwd_chain_rule_across_a_split_run(T1):
+    """Running the sequence as a prefix and a resumed suffix: the suffix's dh0 is
+    the prefix's dhT (the prefix state reaches the loss only through the suffix),
+    and the two backward passes together give the whole run's gradients."""
+    T = 130
+    x = kda_inputs.prefill_inputs(2, T, 3, 128, "bf16", h0=True, seed=37, device=DEV)
+    dO, dhT = upstream(2, T, 3, 128, seed=8)
+    full = run(x, dO, dhT)
+    pre = {n: x[n][:, :T1].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    suf = {n: x[n][:, T1:].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    pre["h0"] = x["h0"]
+    _, h1 = kda.chunk_fwd(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], x["h0"])
+    suf["h0"] = h1
+    gs = run(suf, dO[:, T1:].contiguous(), dhT)
+    gp = run(pre, dO[:, :T1].contiguous(), gs[5])
+    for i, n in enumerate(NAMES[:5]):
+        both = torch.cat([gp[i], gs[i]], dim=1)
+        assert rel_err(both.cpu(), full[i].cpu()) < 1e-3, n
+    assert rel_err(gp[5].cpu(), full[5].cpu()) < 1e-3
+
+
+def test_bwd_linear_in_upstream_gradients():
+    x = kda_inputs.prefill_inputs(1, 70, 2, 128, "bf16", h0=True, seed=38, device=DEV)
+    dO1, dh1 = upstream(1, 70, 2, 128, seed=9)
+    dO2, dh2 = upstream(1, 70, 2, 128, seed=10)
+    g1, g2 = run(x, dO1, dh1), run(x, dO2, dh2)
+    g3 = run(x, 2.0 * dO1 - 0.5 * dO2, 2.0 * dh1 - 0.5 * dh2)
+    for n, a, b, c in zip(NAMES, g1, g2, g3):
+        assert rel_err(c.cpu(), (2.0 * a - 0.5 * b).cpu()) < 1e-4, n
