@@ -8,7 +8,10 @@ Distributions (the workloads the path is measured on):
 
 * q, k ~ N(0, 1), L2-normalised per (batch, token, head) in fp32 with
   ``x / max(||x||, 1e-12)``, then stored in the input dtype (bf16 by
-  round-to-nearest-even, or fp32).
+  round-to-nearest-even, or fp32).  With ``raw_qk`` (inputs of the fused q/k
+  normalisation) they are left unnormalised instead: N(0, 1) per channel
+  times a length factor e^z per (batch, token, head), z ~ N(0, 1), drawn
+  separately for q and k.
 * v ~ N(0, 1), stored in the input dtype.
 * beta = sigmoid(N(0, 1)) per (batch, token, head), fp32.
 * g = g_min * sigmoid(x) per channel with x ~ N(mu, 1), g_min = -5 and mu = 0
@@ -34,7 +37,7 @@ SEGMENT = 65536
 G_MIN = -5.0
 CHUNK = 16
 
-_TID = {"q": 0, "k": 1, "v": 2, "beta": 3, "gate": 4, "h0": 5}
+_TID = {"q": 0, "k": 1, "v": 2, "beta": 3, "gate": 4, "h0": 5, "q_len": 6, "k_len": 7}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -93,16 +96,22 @@ def _unit(x: torch.Tensor) -> torch.Tensor:
     return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-12)
 
 
+def _raw(x: torch.Tensor, seed, tid, seg, device) -> torch.Tensor:
+    return x * torch.exp(_normal(x.shape[:-1] + (1,), seed, tid, seg, device))
+
+
 def fill_prefill_segment(bufs: dict, t0: int, t1: int, *, seed: int, seg: int,
-                         gate_mean: float = 0.0) -> None:
+                         gate_mean: float = 0.0, raw_qk: bool = False) -> None:
     """Draw tokens [t0, t1) of every per-token tensor into ``bufs`` (in place)."""
     q = bufs["q"]
     B, _, H, D = q.shape
     Dv = bufs["v"].shape[-1]
     dev = q.device
     n = t1 - t0
-    bufs["q"][:, t0:t1] = _unit(_normal((B, n, H, D), seed, _TID["q"], seg, dev)).to(q.dtype)
-    bufs["k"][:, t0:t1] = _unit(_normal((B, n, H, D), seed, _TID["k"], seg, dev)).to(q.dtype)
+    for name in ("q", "k"):
+        x = _normal((B, n, H, D), seed, _TID[name], seg, dev)
+        x = _raw(x, seed, _TID[name + "_len"], seg, dev) if raw_qk else _unit(x)
+        bufs[name][:, t0:t1] = x.to(q.dtype)
     bufs["v"][:, t0:t1] = _normal((B, n, H, Dv), seed, _TID["v"], seg, dev).to(q.dtype)
     bufs["beta"][:, t0:t1] = torch.sigmoid(_normal((B, n, H), seed, _TID["beta"], seg, dev))
     x = _normal((B, n, H, D), seed, _TID["gate"], seg, dev, mean=gate_mean)
@@ -114,13 +123,14 @@ def fill_prefill_segment(bufs: dict, t0: int, t1: int, *, seed: int, seg: int,
 def prefill_inputs(B: int, T: int, H: int, D: int, dtype: str = "bf16", *,
                    h0: bool = False, seed: int = 0, device="cpu",
                    gate_mean: float = 0.0, Dv: int | None = None,
-                   gate_logits: str | None = None) -> dict:
+                   gate_logits: str | None = None, raw_qk: bool = False) -> dict:
     """Allocate and draw a full prefill input set.
 
     Returns a dict with q, k, v ([B, T, H, D], dtype), g ([B, T, H, D], fp32),
     beta ([B, T, H], fp32) and h0 ([B, H, D, Dv] fp32, or None).  With
     ``gate_logits`` ("f32" or "bf16") it also holds x, the gate logits g is
-    drawn from, stored in that dtype.
+    drawn from, stored in that dtype.  ``raw_qk`` leaves q and k unnormalised
+    (see the module docstring).
     """
     Dv = D if Dv is None else Dv
     td = torch_dtype(dtype)
@@ -134,7 +144,8 @@ def prefill_inputs(B: int, T: int, H: int, D: int, dtype: str = "bf16", *,
     if gate_logits is not None:
         bufs["x"] = torch.empty((B, T, H, D), dtype=torch_dtype(gate_logits), device=device)
     for seg, t0 in enumerate(range(0, T, SEGMENT)):
-        fill_prefill_segment(bufs, t0, min(T, t0 + SEGMENT), seed=seed, seg=seg, gate_mean=gate_mean)
+        fill_prefill_segment(bufs, t0, min(T, t0 + SEGMENT), seed=seed, seg=seg, gate_mean=gate_mean,
+                             raw_qk=raw_qk)
     bufs["h0"] = _normal((B, H, D, Dv), seed, _TID["h0"], 0, device, std=0.1) if h0 else None
     return bufs
 
@@ -146,14 +157,19 @@ def config_inputs(cfg: PrefillConfig, device="cpu", T: int | None = None) -> dic
 
 
 def decode_inputs(B: int, H: int, D: int, dtype: str = "bf16", *, seed: int = 0,
-                  device="cpu", gate_mean: float = 0.0, Dv: int | None = None) -> dict:
+                  device="cpu", gate_mean: float = 0.0, Dv: int | None = None, raw_qk: bool = False) -> dict:
     """One new token per sequence: q, k, v [B, H, D]; g [B, H, D]; beta [B, H];
     state [B, H, D, Dv] ~ N(0, 0.01), all drawn as for prefill."""
     Dv = D if Dv is None else Dv
     td = torch_dtype(dtype)
+
+    def qk(name):
+        x = _normal((B, H, D), seed, _TID[name], 0, device)
+        return (_raw(x, seed, _TID[name + "_len"], 0, device) if raw_qk else _unit(x)).to(td)
+
     return {
-        "q": _unit(_normal((B, H, D), seed, _TID["q"], 0, device)).to(td),
-        "k": _unit(_normal((B, H, D), seed, _TID["k"], 0, device)).to(td),
+        "q": qk("q"),
+        "k": qk("k"),
         "v": _normal((B, H, Dv), seed, _TID["v"], 0, device).to(td),
         "beta": torch.sigmoid(_normal((B, H), seed, _TID["beta"], 0, device)),
         "g": G_MIN * torch.sigmoid(_normal((B, H, D), seed, _TID["gate"], 0, device, mean=gate_mean)),

@@ -100,6 +100,26 @@ def gate_from_logit(x, g_min: float = -5.0) -> np.ndarray:
         return g_min / (1.0 + np.exp(-x))
 
 
+def l2_normalize(x, eps: float = 1e-12) -> np.ndarray:
+    """Every vector along the last axis divided by its Euclidean length, in
+    fp64: ``x / max(||x||_2, eps)``.  A zero vector stays zero; a vector
+    shorter than ``eps`` is divided by ``eps``.
+
+    The q/k normalisation in front of the recurrence.  The pages do not write
+    it out.  Reading: the erase-then-write step with the incoming key
+    ("Kimi K3 Architecture Explained", section 3, the DeltaNet eraser) removes
+    exactly the recalled value only for a unit key, and the bound on the
+    state that the bounded gate of the Kimi K3 paper digest (devpress.csdn.net,
+    section 2.1 (1)) protects assumes keys of bounded length; so keys (and,
+    as is usual for delta-rule attention, queries) are unit vectors, with the
+    floor ``eps`` keeping a zero vector finite.  ``x`` is taken exactly as
+    stored (bf16 or fp32 converted to fp64).
+    """
+    x = _f64(x.float().cpu().numpy() if hasattr(x, "float") else x)
+    length = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(length, eps)
+
+
 def kda_fwd(q, k, v, g, beta, h0=None, scale=None):
     """Token-sequential KDA forward in fp64 (C implementation).
 

@@ -42,6 +42,22 @@ def test_distributions():
     assert abs(x["g"].mean().item() + 2.5) < 0.05
 
 
+def test_raw_qk_keeps_the_direction():
+    # raw q, k are the same N(0, 1) draws as the normalised ones, times a
+    # per-token length factor e^z: same directions, spread-out lengths
+    a = kda_inputs.prefill_inputs(1, 256, 3, 128, "f32", seed=3)
+    b = kda_inputs.prefill_inputs(1, 256, 3, 128, "f32", seed=3, raw_qk=True)
+    for n in ("q", "k"):
+        ln = b[n].norm(dim=-1, keepdim=True)
+        assert (b[n] / ln - a[n]).abs().max() < 1e-5
+        z = torch.log(ln / 128 ** 0.5)  # about N(0, 1), with the chi spread of the N(0, 1) length on top
+        assert abs(z.mean().item()) < 0.2 and 0.8 < z.std().item() < 1.2
+    for n in ("v", "beta", "g"):
+        assert torch.equal(a[n], b[n])
+    d = kda_inputs.decode_inputs(4, 2, 16, "bf16", seed=4, raw_qk=True)
+    assert (d["k"].float().norm(dim=-1) - 1).abs().max() > 0.1
+
+
 def test_gate_range_from_pages():
     fx = json.load(open(GOLDEN))
     g_min, C = fx["g_min"], fx["chunk"]

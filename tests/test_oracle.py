@@ -198,3 +198,83 @@ def test_gate_takes_bf16_logits_as_stored():
     x = torch.tensor([0.1, -1.7, 3.3], dtype=torch.bfloat16)
     xs = x.float().double().numpy()  # the stored bf16 values, exactly
     assert np.array_equal(oracle.gate_from_logit(x, -5.0), -5.0 / (1.0 + np.exp(-xs)))
+
+
+# ---- the q/k normalisation prologue: x / max(||x||, eps) along the last axis ----
+
+def _l2_pin_closed_forms(f):
+    y = f(np.array([[3.0, 4.0], [0.0, -2.0], [0.0, 0.0]]), 1e-12)
+    assert np.array_equal(y, np.array([[0.6, 0.8], [0.0, -1.0], [0.0, 0.0]]))  # 3-4-5 triangle; zero stays zero
+
+
+def _l2_pin_eps_floor(f):
+    # a vector shorter than eps is divided by eps, not by its length
+    y = f(np.array([3e-13, 4e-13]), 1e-12)
+    assert np.allclose(y, [0.3, 0.4], rtol=1e-14, atol=0)
+    y = f(np.array([3.0, 4.0]), 10.0)
+    assert np.allclose(y, [0.3, 0.4], rtol=1e-15, atol=0)
+
+
+def _l2_pin_unit_length_and_direction(f):
+    x = np.random.default_rng(9).normal(size=(5, 7, 33)) * np.exp(np.random.default_rng(10).uniform(-3, 3, (5, 7, 1)))
+    y = f(x, 1e-12)
+    assert np.max(np.abs(np.sqrt((y * y).sum(-1)) - 1.0)) < 1e-14
+    # parallel to x with a positive factor: y . x = ||x||
+    assert np.max(np.abs((y * x).sum(-1) - np.sqrt((x * x).sum(-1)))) < 1e-12 * np.max(np.abs(x))
+
+
+def _l2_pin_last_axis_only(f):
+    # rows are independent, and the length is taken over the last axis
+    x = np.array([[1.0, 0.0, 0.0, 0.0], [0.0, 2.0, 0.0, 0.0], [1.0, 1.0, 1.0, 1.0]])
+    y = f(x, 1e-12)
+    assert np.array_equal(y, np.array([[1.0, 0, 0, 0], [0, 1.0, 0, 0], [0.5, 0.5, 0.5, 0.5]]))
+
+
+def _l2_pin_invariances(f):
+    x = np.random.default_rng(11).normal(size=(4, 16))
+    y = f(x, 1e-12)
+    assert np.max(np.abs(f(7.5 * x, 1e-12) - y)) < 1e-15   # positive scaling
+    assert np.array_equal(f(-x, 1e-12), -y)                 # odd
+    assert np.max(np.abs(f(y, 1e-12) - y)) < 1e-15          # idempotent
+
+
+L2_PINS = [_l2_pin_closed_forms, _l2_pin_eps_floor, _l2_pin_unit_length_and_direction, _l2_pin_last_axis_only,
+           _l2_pin_invariances]
+
+
+@pytest.mark.parametrize("pin", L2_PINS, ids=lambda p: p.__name__)
+def test_l2_normalize_pin(pin):
+    pin(oracle.l2_normalize)
+
+
+_L2_MUTANTS = {
+    "squared_length": lambda x, eps: x / np.maximum((x * x).sum(-1, keepdims=True), eps),
+    "l1_length": lambda x, eps: x / np.maximum(np.abs(x).sum(-1, keepdims=True), eps),
+    "eps_added": lambda x, eps: x / (np.sqrt((x * x).sum(-1, keepdims=True)) + 1e-3 * (eps > 0)),
+    "first_axis": lambda x, eps: x / np.maximum(np.sqrt((x * x).sum(0, keepdims=True)), eps),
+    "no_floor": lambda x, eps: x / np.sqrt((x * x).sum(-1, keepdims=True) + 1e-300),
+    "eps_floor_squared": lambda x, eps: x / np.maximum(np.sqrt((x * x).sum(-1, keepdims=True)), eps * eps),
+}
+
+
+@pytest.mark.parametrize("kind", sorted(_L2_MUTANTS))
+def test_l2_planted_mistake_is_caught(kind):
+    f = _L2_MUTANTS[kind]
+    failed = []
+    for pin in L2_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(f)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, "mutant %s passed every pin" % kind
+
+
+def test_l2_normalize_takes_bf16_as_stored():
+    import torch
+
+    x = torch.tensor([[0.1, -1.7, 3.3]], dtype=torch.bfloat16)
+    xs = x.float().double().numpy()
+    y = oracle.l2_normalize(x)
+    assert y.dtype == np.float64
+    assert np.max(np.abs(y * np.sqrt((xs * xs).sum()) - xs)) < 1e-15
