@@ -83,7 +83,7 @@ def load_traffic(kernel="prefill"):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    pre = kernel in ("prefill", "gate")  # the plain and fused-gate prefill share their sources
+    pre = kernel in ("prefill", "gate", "qknorm")  # the prefill variants share their sources
     sha = t.get("kernel_src_sha") if pre else t.get("decode_src_sha")
     if sha != source_hash(KERNEL_SOURCES if pre else DECODE_SOURCES):
         return None
@@ -315,6 +315,8 @@ def main():
     ap.add_argument("--segmented-only", action="store_true",
                     help="time only the segmented prefill (for a kernel trace of its launches alone)")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
+    ap.add_argument("--no-qknorm", action="store_true",
+                    help="skip timing the prefill and decode step with the fused q/k normalisation")
     ap.add_argument("--no-host-cost", action="store_true",
                     help="skip the host cost per decode call (its small launches would mix into a kernel trace)")
     ap.add_argument("--no-configs", action="store_true",
@@ -450,6 +452,17 @@ def main():
             gate_ev[i][1].record(stream)
         torch.cuda.synchronize()
         gate_ms = [e[0].elapsed_time(e[1]) for e in gate_ev]
+    qkn = None
+    if not args.no_qknorm:
+        # the fused q/k normalisation: the same workloads and the same bytes
+        # (q and k are read once either way); the generator's q and k are unit
+        # vectors, which changes nothing in the work done
+        log("q/k normalisation")
+        qkn = {"prefill": time_launches(torch, stream, lambda: kda.chunk_fwd_qknorm(
+            x["q"], x["k"], x["v"], x["g"], x["beta"], None, eps=1e-6, o=o, hT=hT, stream=stream), args.steps)}
+        if d is not None:
+            qkn["decode"] = time_launches(torch, stream, lambda: kda.decode_step_qknorm(
+                d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], eps=1e-6, o=od, stream=stream), args.steps)
     seg = None
     if args.segments > 0:
         seg = time_segmented(kda, torch, stream, args.segments, args.steps)
@@ -508,6 +521,20 @@ def main():
                                 "vs_log_decay_entry": g_avg / pre_avg, "achieved": g_ach, "peak": HBM_PEAK_GBPS,
                                 "unit": "GB/s", "frac": g_ach / HBM_PEAK_GBPS, "alg_bytes_per_launch": g_bytes,
                                 "traffic": load_traffic("gate") if gate_dt == "bf16" else None}
+    if qkn is not None:
+        q_avg, q_min = qkn["prefill"]
+        q_ach = pbytes / (q_avg * 1e-3) / 1e9
+        result["qknorm"] = {"workload": cfg.name + "_qknorm", "ms": q_avg, "min_ms": q_min,
+                            "vs_plain_entry": q_avg / pre_avg, "achieved": q_ach, "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": q_ach / HBM_PEAK_GBPS, "alg_bytes_per_launch": pbytes,
+                            "traffic": load_traffic("qknorm")}
+        if "decode" in qkn:
+            dq_avg, dq_min = qkn["decode"]
+            dq_bytes = decode_bytes(dcfg.B, dcfg.H, dcfg.D, 2)
+            dq_ach = dq_bytes / (dq_avg * 1e-3) / 1e9
+            result["qknorm"]["decode"] = {"workload": dcfg.name + "_qknorm", "ms": dq_avg, "min_ms": dq_min,
+                                          "achieved": dq_ach, "frac": dq_ach / HBM_PEAK_GBPS,
+                                          "alg_bytes_per_launch": dq_bytes, "traffic": load_traffic("decode_qknorm")}
     if seg is not None:
         result["segmented"] = seg
     result["copy"] = copy_bandwidth(torch, stream)

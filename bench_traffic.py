@@ -38,6 +38,8 @@ import bench
 PREFILL = "prefill_mfma_kernel<false, 0, 0>" # plain prefill (fp32 log-decay gate)
 GATE = "prefill_mfma_kernel<false, 2, 0>"    # fused gate prologue, bf16 logits
 DECODE = "decode_kernel"
+QKNORM = "prefill_mfma_qknorm_kernel<0>"  # the prefill with the fused q/k normalisation
+DECODE_QKNORM = "decode_qknorm_kernel"
 COPY = "copyBuffer"
 
 
@@ -105,7 +107,8 @@ def main(dt, df, dw, out):
     sf, sw = kib / copy_f, kib / copy_w
     res = {"copy_bytes": bench.COPY_BYTES, "fetch_scale": sf, "write_scale": sw,
            "kernel_src_sha": bench.source_hash(), "decode_src_sha": bench.source_hash(bench.DECODE_SOURCES)}
-    for key, tag in ((PREFILL, "prefill"), (GATE, "gate"), (DECODE, "decode")):
+    for key, tag in ((PREFILL, "prefill"), (GATE, "gate"), (DECODE, "decode"), (QKNORM, "qknorm"),
+                     (DECODE_QKNORM, "decode_qknorm")):
         f, nf = mean_for(fetch, key)
         w, nw = mean_for(write, key)
         if f is None or w is None:
@@ -118,7 +121,7 @@ def main(dt, df, dw, out):
     res["kernel_stats"] = [{"name": r["Name"][:90], "calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
                             "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])}
                            for r in stats if "prefill_mfma_kernel" in r["Name"] or DECODE in r["Name"]
-                           or COPY in r["Name"]]
+                           or "qknorm_kernel" in r["Name"] or COPY in r["Name"]]
     # the launches bench.py times with events (the last TIMED_STEPS of each
     # kernel; the first is the warmup, whose cold start the --stats average
     # includes): their mean is the figure comparable with the bench line
@@ -130,8 +133,9 @@ def main(dt, df, dw, out):
         json.dump(res, f, indent=1)
     alg_p = bench.prefill_bytes(1, 65536, 56, 128)
     alg_d = bench.decode_bytes(256, 56, 128)
-    lines = ["# rocprofv3: KDA prefill (B=1 H=56 T=65536 d=128; fp32 log-decay gate, and bf16 gate logits with "
-             "the fused gate prologue) and decode (B=256 H=56 d=128)", "",
+    lines = ["# rocprofv3: KDA prefill (B=1 H=56 T=65536 d=128; fp32 log-decay gate, bf16 gate logits with "
+             "the fused gate prologue, and the fused q/k normalisation) and decode (B=256 H=56 d=128, without "
+             "and with the q/k normalisation)", "",
              "Commands (from the repository root):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d DIR_T -o trace -- "
              "python3 bench.py --steps 20 --warmup 1 --no-cpu-baseline --segments 0 --no-configs --no-backward --no-host-cost",
@@ -156,7 +160,8 @@ def main(dt, df, dw, out):
               "| kernel | raw fetch KiB | raw write KiB | scaled bytes | algorithmic bytes | ratio |",
               "|---|---|---|---|---|---|"]
     alg_g = bench.prefill_bytes(1, 65536, 56, 128, gate_bytes=2)
-    for tag, alg in (("prefill", alg_p), ("gate", alg_g), ("decode", alg_d)):
+    for tag, alg in (("prefill", alg_p), ("gate", alg_g), ("decode", alg_d), ("qknorm", alg_p),
+                     ("decode_qknorm", alg_d)):
         if tag not in res:
             continue
         r = res[tag]
@@ -265,7 +270,7 @@ def utilisation(du, out, cus=256, simds_per_cu=4, xcds=8):
     """Issue and pipe-busy summary of the plain prefill from one counter run:
 
     rocprofv3 --pmc <UTIL_COUNTERS> --output-format csv -d DIR_U -o util -- \
-        python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --no-configs --no-backward --no-host-cost --no-decode --gate-logits none
+        python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --no-configs --no-backward --no-host-cost --no-decode --gate-logits none --no-qknorm
     """
     import collections
     rows = _csv(du, "counter_collection.csv")
@@ -281,7 +286,7 @@ def utilisation(du, out, cus=256, simds_per_cu=4, xcds=8):
     wgs = 56 * 4
     per_chunk_simd = lambda c: m[c] / (wgs * simds_per_cu * steps)
     cmd = ("rocprofv3 --pmc %s --output-format csv -d DIR_U -o util -- python3 bench.py --steps 2 --warmup 1 "
-           "--no-cpu-baseline --segments 0 --no-configs --no-backward --no-host-cost --no-decode --gate-logits none" % UTIL_COUNTERS)
+           "--no-cpu-baseline --segments 0 --no-configs --no-backward --no-host-cost --no-decode --gate-logits none --no-qknorm" % UTIL_COUNTERS)
     lines = ["# rocprofv3: KDA prefill (B=1 H=56 T=65536 d=128) issue and pipe utilisation", "",
              "Commands (from the repository root):", "", "    " + cmd,
              "    python3 bench_traffic.py --util DIR_U profiles", "",

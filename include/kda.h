@@ -67,6 +67,13 @@ typedef enum kda_dtype {
     KDA_BF16 = 1
 } kda_dtype;
 
+/* How the forget gate is given to kda_chunk_fwd_qknorm. */
+typedef enum kda_gate {
+    KDA_GATE_LOG_DECAY = 0,  /* g itself, fp32 (as kda_chunk_fwd) */
+    KDA_GATE_LOGIT_F32 = 1,  /* fp32 logits x, g = g_min sigmoid(x) (as kda_chunk_fwd_gate) */
+    KDA_GATE_LOGIT_BF16 = 2  /* bf16 logits x, likewise */
+} kda_gate;
+
 /*
  * kda_chunk_fwd -- chunked prefill over a whole sequence, with an optional
  * initial state (prefix reuse: the digest's section 2.4 (4) keeps sparse KDA
@@ -142,6 +149,36 @@ kda_status kda_chunk_fwd_gate(const void *q, const void *k, const void *v,
                               float *o, float *hT,
                               int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
                               kda_dtype in_dtype, float scale, void *stream);
+
+/*
+ * kda_chunk_fwd_qknorm -- the prefill with the q/k normalisation fused in
+ * front of it: every query and key vector (per batch row, token and head) is
+ * used as
+ *
+ *   x / max(||x||_2, eps)
+ *
+ * formed in fp32 from the stored values inside the kernel, so the raw
+ * projections go in unchanged and no normalised copy is written.  The pages
+ * name no normalisation; the erase-then-write with the incoming key
+ * ("Kimi K3 Architecture Explained", section 3) removes the recalled value
+ * exactly only for a unit key, which is why delta-rule layers feed unit keys
+ * (and queries).
+ *
+ *   g, gate    the gate as kda_chunk_fwd's g (KDA_GATE_LOG_DECAY; g_min is
+ *              then ignored) or as kda_chunk_fwd_gate's logits x (the two
+ *              KDA_GATE_LOGIT kinds, with g_min as there)
+ *   eps        the floor, finite and 1e-18 <= eps <= 1e18, else
+ *              KDA_ERR_INVALID_ARGUMENT (a zero vector stays zero)
+ *
+ * All other arguments, the layouts and the errors are those of kda_chunk_fwd
+ * (g takes the place of kda_chunk_fwd's g or kda_chunk_fwd_gate's x).
+ */
+kda_status kda_chunk_fwd_qknorm(const void *q, const void *k, const void *v,
+                                const void *g, kda_gate gate, float g_min, float eps,
+                                const float *beta, const float *h0,
+                                float *o, float *hT,
+                                int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                kda_dtype in_dtype, float scale, void *stream);
 
 /*
  * kda_chunk_fwd_kcp -- kda_chunk_fwd computed as n_seg segments in parallel:
@@ -281,6 +318,18 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            float *state, float *o,
                            int64_t B, int64_t H, int64_t Dk, int64_t Dv,
                            kda_dtype in_dtype, float scale, void *stream);
+
+/*
+ * kda_decode_step_qknorm -- kda_decode_step with q and k normalised as in
+ * kda_chunk_fwd_qknorm (x / max(||x||_2, eps), in fp32, inside the kernel).
+ * eps: finite, 1e-18 <= eps <= 1e18, else KDA_ERR_INVALID_ARGUMENT.  All
+ * other arguments, the layouts and the errors are those of kda_decode_step.
+ */
+kda_status kda_decode_step_qknorm(const void *q, const void *k, const void *v,
+                                  const float *g, const float *beta,
+                                  float *state, float *o,
+                                  int64_t B, int64_t H, int64_t Dk, int64_t Dv,
+                                  kda_dtype in_dtype, float scale, float eps, void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *kda_status_string(kda_status s);

@@ -16,7 +16,9 @@ import threading
 
 import torch
 
-__all__ = ["chunk_bwd", "bwd_ws_bytes", "chunk_fwd", "chunk_fwd_ckpt", "chunk_fwd_gate", "chunk_fwd_kcp", "chunk_fwd_kcp_noalloc", "kcp_ws_bytes", "decode_step", "KdaError", "library", "library_path", "version"]
+__all__ = ["chunk_bwd", "bwd_ws_bytes", "chunk_fwd", "chunk_fwd_ckpt", "chunk_fwd_gate", "chunk_fwd_kcp",
+           "chunk_fwd_kcp_noalloc", "chunk_fwd_qknorm", "kcp_ws_bytes", "decode_step", "decode_step_qknorm",
+           "KdaError", "library", "library_path", "version"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -26,6 +28,9 @@ _lib = None
 KDA_OK = 0
 KDA_F32 = 0
 KDA_BF16 = 1
+KDA_GATE_LOG_DECAY = 0
+KDA_GATE_LOGIT_F32 = 1
+KDA_GATE_LOGIT_BF16 = 2
 
 
 class KdaError(RuntimeError):
@@ -58,6 +63,10 @@ def library() -> ctypes.CDLL:
             lib.kda_chunk_fwd_gate.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_float, fp, fp, fp, fp,
                                                i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, vp]
             lib.kda_chunk_fwd_gate.restype = ctypes.c_int
+            lib.kda_chunk_fwd_qknorm.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_float, ctypes.c_float, fp,
+                                                 fp, fp, fp, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                                                 vp]
+            lib.kda_chunk_fwd_qknorm.restype = ctypes.c_int
             lib.kda_chunk_fwd_kcp.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, i64, vp, ctypes.c_uint64,
                                               i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, vp]
             lib.kda_chunk_fwd_kcp.restype = ctypes.c_int
@@ -76,6 +85,9 @@ def library() -> ctypes.CDLL:
             lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, i64, i64, i64, i64,
                                             ctypes.c_int, ctypes.c_float, vp]
             lib.kda_decode_step.restype = ctypes.c_int
+            lib.kda_decode_step_qknorm.argtypes = [vp, vp, vp, fp, fp, fp, fp, i64, i64, i64, i64,
+                                                   ctypes.c_int, ctypes.c_float, ctypes.c_float, vp]
+            lib.kda_decode_step_qknorm.restype = ctypes.c_int
             lib.kda_status_string.argtypes = [ctypes.c_int]
             lib.kda_status_string.restype = ctypes.c_char_p
             lib.kda_last_error.argtypes = []
@@ -194,6 +206,49 @@ def chunk_fwd_gate(q, k, v, x, beta, h0=None, *, g_min: float = -5.0, scale: flo
     _check(lib.kda_chunk_fwd_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(x), _dtype_code(x), float(g_min), _ptr(beta),
                                   _ptr(h0), _ptr(o), _ptr(hT), B, T, H, Dk, Dv, _dtype_code(q),
                                   float(scale or 0.0), _stream(stream)))
+    return o, hT
+
+
+def chunk_fwd_qknorm(q, k, v, g, beta, h0=None, *, eps: float = 1e-12, gate_logits: bool = False,
+                     g_min: float = -5.0, scale: float | None = None, o=None, hT=None,
+                     output_final_state: bool = True, stream=None):
+    """Chunked KDA prefill with q and k normalised in the kernel (``kda_chunk_fwd_qknorm``).
+
+    q and k are the raw (unnormalised) vectors; each is used as
+    x / max(||x||, eps).  g is the fp32 log-decay, or with ``gate_logits`` the
+    gate logits (fp32 or bf16) with g = g_min * sigmoid(x).  Everything else
+    as :func:`chunk_fwd`.
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    if gate_logits:
+        _need(g, "g")
+        gate = KDA_GATE_LOGIT_BF16 if _dtype_code(g) == KDA_BF16 else KDA_GATE_LOGIT_F32
+    else:
+        _need(g, "g", torch.float32)
+        gate = KDA_GATE_LOG_DECAY
+    _need(beta, "beta", torch.float32)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.float32)
+    if hT is None and output_final_state:
+        hT = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if hT is not None:
+        _need(hT, "hT", torch.float32)
+    shapes_ok = (k.shape == q.shape and g.shape == q.shape and v.shape[:3] == (B, T, H)
+                 and beta.shape == (B, T, H) and o.shape == (B, T, H, Dv)
+                 and (h0 is None or h0.shape == (B, H, Dk, Dv))
+                 and (hT is None or hT.shape == (B, H, Dk, Dv)))
+    if not shapes_ok:
+        raise ValueError("inconsistent shapes")
+    lib = library()
+    _check(lib.kda_chunk_fwd_qknorm(_ptr(q), _ptr(k), _ptr(v), _ptr(g), gate, float(g_min), float(eps), _ptr(beta),
+                                    _ptr(h0), _ptr(o), _ptr(hT), B, T, H, Dk, Dv, _dtype_code(q),
+                                    float(scale or 0.0), _stream(stream)))
     return o, hT
 
 
@@ -400,4 +455,28 @@ def decode_step(q, k, v, g, beta, state, *, scale: float | None = None, o=None, 
     lib = library()
     _check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
                                B, H, Dk, Dv, _dtype_code(q), float(scale or 0.0), _stream(stream)))
+    return o
+
+
+def decode_step_qknorm(q, k, v, g, beta, state, *, eps: float = 1e-12, scale: float | None = None, o=None,
+                       stream=None):
+    """:func:`decode_step` with q and k normalised in the kernel (``kda_decode_step_qknorm``):
+    each is used as x / max(||x||, eps)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32)
+    _need(state, "state", torch.float32)
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, H, Dv), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.float32)
+    if not (k.shape == q.shape and g.shape == q.shape and v.shape[:2] == (B, H) and beta.shape == (B, H)
+            and state.shape == (B, H, Dk, Dv) and o.shape == (B, H, Dv)):
+        raise ValueError("inconsistent shapes")
+    lib = library()
+    _check(lib.kda_decode_step_qknorm(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+                                      B, H, Dk, Dv, _dtype_code(q), float(scale or 0.0), float(eps),
+                                      _stream(stream)))
     return o

@@ -135,11 +135,13 @@ kda_status launch_prefill(const kda::PrefillArgs &a, hipStream_t s) {
 }
 
 // The prefill entry points: kda_chunk_fwd is this with no checkpoints.  With
-// `out`, the validated arguments are returned instead of launched.
+// `out`, the validated arguments are returned instead of launched.  qk_eps > 0
+// turns on the q/k normalisation with that floor (checked by the caller).
 kda_status chunk_fwd(const void *q, const void *k, const void *v, const void *g, kda::GateMode gate, float g_min,
                      const float *beta, const float *h0, float *o, float *hT, float *ckpt, int64_t ckpt_every,
                      int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale,
-                     void *stream, kda::PrefillArgs *out = nullptr, bool device_checks = true) {
+                     void *stream, kda::PrefillArgs *out = nullptr, bool device_checks = true,
+                     float qk_eps = 0.f) {
     if (B <= 0 || H <= 0 || Dk <= 0 || Dv <= 0 || T < 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "sizes must be positive (T >= 0): B=%lld T=%lld H=%lld Dk=%lld Dv=%lld",
                     (long long)B, (long long)T, (long long)H, (long long)Dk, (long long)Dv);
@@ -206,6 +208,8 @@ kda_status chunk_fwd(const void *q, const void *k, const void *v, const void *g,
     a.bf16 = in_dtype == KDA_BF16;
     a.scale = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(Dk));
     a.epoch = 0;
+    a.qk_norm = qk_eps > 0.f;
+    a.qk_eps2 = qk_eps * qk_eps;
     if (out) {
         *out = a;
         return ok();
@@ -244,6 +248,25 @@ kda_status kda_chunk_fwd_gate(const void *q, const void *k, const void *v, const
     const kda::GateMode gate = gate_dtype == KDA_BF16 ? kda::kGateLogitBf16 : kda::kGateLogitF32;
     return chunk_fwd(q, k, v, x, gate, g_min, beta, h0, o, hT, nullptr, 0, B, T, H, Dk, Dv, in_dtype, scale,
                      stream);
+}
+
+kda_status kda_chunk_fwd_qknorm(const void *q, const void *k, const void *v, const void *g, kda_gate gate,
+                                float g_min, float eps, const float *beta, const float *h0, float *o, float *hT,
+                                int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype,
+                                float scale, void *stream) {
+    kda::GateMode mode;
+    switch (gate) {
+        case KDA_GATE_LOG_DECAY: mode = kda::kGateLogDecay; break;
+        case KDA_GATE_LOGIT_F32: mode = kda::kGateLogitF32; break;
+        case KDA_GATE_LOGIT_BF16: mode = kda::kGateLogitBf16; break;
+        default: return fail(KDA_ERR_INVALID_ARGUMENT, "unknown gate kind %d", static_cast<int>(gate));
+    }
+    if (mode != kda::kGateLogDecay && !(g_min >= -5.f && g_min < 0.f))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "g_min=%g must satisfy -5 <= g_min < 0", static_cast<double>(g_min));
+    if (!(eps >= 1e-18f && eps <= 1e18f))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "eps=%g must lie in [1e-18, 1e18]", static_cast<double>(eps));
+    return chunk_fwd(q, k, v, g, mode, mode == kda::kGateLogDecay ? 0.f : g_min, beta, h0, o, hT, nullptr, 0, B, T,
+                     H, Dk, Dv, in_dtype, scale, stream, nullptr, true, eps);
 }
 
 uint64_t kda_chunk_fwd_kcp_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t n_seg) {
@@ -451,9 +474,14 @@ kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const floa
     return launch_status(kda::launch_bwd(a, s), "kda backward");
 }
 
-kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                           float *state, float *o, int64_t B, int64_t H, int64_t Dk, int64_t Dv,
-                           kda_dtype in_dtype, float scale, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode entry points; qk_eps > 0 turns on the q/k normalisation.
+kda_status decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                       float *state, float *o, int64_t B, int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype,
+                       float scale, float qk_eps, void *stream) {
     if (B <= 0 || H <= 0 || Dk <= 0 || Dv <= 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "sizes must be positive: B=%lld H=%lld Dk=%lld Dv=%lld",
                     (long long)B, (long long)H, (long long)Dk, (long long)Dv);
@@ -493,7 +521,27 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const fl
     a.B = B; a.H = H; a.D = static_cast<int>(Dk);
     a.bf16 = in_dtype == KDA_BF16;
     a.scale = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(Dk));
+    a.qk_norm = qk_eps > 0.f;
+    a.qk_eps2 = qk_eps * qk_eps;
     return launch_status(kda::launch_decode(a, static_cast<hipStream_t>(stream)), "kda decode");
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                           float *state, float *o, int64_t B, int64_t H, int64_t Dk, int64_t Dv,
+                           kda_dtype in_dtype, float scale, void *stream) {
+    return decode_step(q, k, v, g, beta, state, o, B, H, Dk, Dv, in_dtype, scale, 0.f, stream);
+}
+
+kda_status kda_decode_step_qknorm(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                                  float *state, float *o, int64_t B, int64_t H, int64_t Dk, int64_t Dv,
+                                  kda_dtype in_dtype, float scale, float eps, void *stream) {
+    if (!(eps >= 1e-18f && eps <= 1e18f))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "eps=%g must lie in [1e-18, 1e18]", static_cast<double>(eps));
+    return decode_step(q, k, v, g, beta, state, o, B, H, Dk, Dv, in_dtype, scale, eps, stream);
 }
 
 }  // extern "C"

@@ -15,6 +15,12 @@
 // while the current one is reduced and written back, so reads and writes of
 // consecutive heads overlap.  The two column reductions (r, p) and k . q are
 // combined across row groups through LDS.
+//
+// With the q/k normalisation (NORM), the sums of squares of q and k are
+// combined the same way, and the factors c = 1 / max(||k||, eps) and
+// d = 1 / max(||q||, eps) are applied where the raw vectors enter:
+//   r = c S'^T k,  e = beta (v - r),  S_new = S' + k (c e)^T,
+//   o = scale * d * (S'^T q + (c e) (k . q)).
 #include <atomic>
 
 #include "kda_internal.h"
@@ -32,8 +38,8 @@ struct DecodeShape {
     static constexpr int RPT = D / RG;                              // rows per thread
 };
 
-template <int D, typename InT>
-__global__ __launch_bounds__(DecodeShape<D>::NT) void decode_kernel(DecodeArgs a) {
+template <int D, typename InT, bool NORM>
+__device__ __forceinline__ void decode_body(DecodeArgs a) {
     using Sh = DecodeShape<D>;
     constexpr int NQ = Sh::NQ, RG = Sh::RG, RPT = Sh::RPT;
     static_assert(RG * RPT == D && NQ * RG == Sh::NT, "bad decode tiling");
@@ -41,6 +47,7 @@ __global__ __launch_bounds__(DecodeShape<D>::NT) void decode_kernel(DecodeArgs a
     __shared__ f32x4 sR[2][RG][NQ];
     __shared__ f32x4 sP[2][RG][NQ];
     __shared__ float sKQ[2][RG];
+    __shared__ float sNrm[NORM ? 2 : 1][2][RG];  // sums of squares [par][q, k][row group]
     __shared__ f32x4 sE[2][NQ];
 
     const int tid = threadIdx.x;
@@ -72,7 +79,7 @@ __global__ __launch_bounds__(DecodeShape<D>::NT) void decode_kernel(DecodeArgs a
 
         float kk[RPT];
         f32x4 r4 = {0.f, 0.f, 0.f, 0.f}, p4 = r4;
-        float kq = 0.f;
+        float kq = 0.f, qq = 0.f, k2 = 0.f;
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             const int i = rg + RG * m;
@@ -84,26 +91,47 @@ __global__ __launch_bounds__(DecodeShape<D>::NT) void decode_kernel(DecodeArgs a
             r4 += ki * s[m];
             p4 += qi * s[m];
             kq += ki * qi;
+            if constexpr (NORM) {
+                qq += qi * qi;
+                k2 += ki * ki;
+            }
         }
         sR[par][rg][jq] = r4;
         sP[par][rg][jq] = p4;
-        if (jq == 0) sKQ[par][rg] = kq;
+        if (jq == 0) {
+            sKQ[par][rg] = kq;
+            if constexpr (NORM) {
+                sNrm[par][0][rg] = qq;
+                sNrm[par][1][rg] = k2;
+            }
+        }
         __syncthreads();
 
         if (rg == 0) {
             f32x4 rt = {0.f, 0.f, 0.f, 0.f}, pt = rt;
-            float kqt = 0.f;
+            float kqt = 0.f, qqt = 0.f, k2t = 0.f;
             for (int j = 0; j < RG; ++j) {
                 rt += sR[par][j][jq];
                 pt += sP[par][j][jq];
                 kqt += sKQ[par][j];
+                if constexpr (NORM) {
+                    qqt += sNrm[par][0][j];
+                    k2t += sNrm[par][1][j];
+                }
             }
             const float bt = a.beta[bh];
             const int c0 = jq * 4;
             const f32x4 vv = {ld_elem(v, c0 + 0), ld_elem(v, c0 + 1), ld_elem(v, c0 + 2), ld_elem(v, c0 + 3)};
-            const f32x4 e = bt * (vv - rt);
-            sE[par][jq] = e;
-            reinterpret_cast<f32x4 *>(a.o + bh * D)[jq] = a.scale * (pt + e * kqt);
+            if constexpr (NORM) {
+                const float c = norm_factor(k2t, a.qk_eps2), d = norm_factor(qqt, a.qk_eps2);
+                const f32x4 e = c * (bt * (vv - c * rt));  // c e: the write along the raw k
+                sE[par][jq] = e;
+                reinterpret_cast<f32x4 *>(a.o + bh * D)[jq] = (a.scale * d) * (pt + e * kqt);
+            } else {
+                const f32x4 e = bt * (vv - rt);
+                sE[par][jq] = e;
+                reinterpret_cast<f32x4 *>(a.o + bh * D)[jq] = a.scale * (pt + e * kqt);
+            }
         }
         __syncthreads();
 
@@ -115,6 +143,16 @@ __global__ __launch_bounds__(DecodeShape<D>::NT) void decode_kernel(DecodeArgs a
             for (int m = 0; m < RPT; ++m) s[m] = sn[m];
         }
     }
+}
+
+template <int D, typename InT>
+__global__ __launch_bounds__(DecodeShape<D>::NT) void decode_kernel(DecodeArgs a) {
+    decode_body<D, InT, false>(a);
+}
+// With the q/k normalisation (a kernel of its own name for kernel traces).
+template <int D, typename InT>
+__global__ __launch_bounds__(DecodeShape<D>::NT) void decode_qknorm_kernel(DecodeArgs a) {
+    decode_body<D, InT, true>(a);
 }
 
 // Work-groups resident at once: four per compute unit keeps enough state
@@ -136,8 +174,12 @@ int decode_grid(int64_t BH) {
 template <int D>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(decode_grid(a.B * a.H))), block(DecodeShape<D>::NT);
-    if (a.bf16)
+    if (a.bf16 && a.qk_norm)
+        hipLaunchKernelGGL((decode_qknorm_kernel<D, uint16_t>), grid, block, 0, s, a);
+    else if (a.bf16)
         hipLaunchKernelGGL((decode_kernel<D, uint16_t>), grid, block, 0, s, a);
+    else if (a.qk_norm)
+        hipLaunchKernelGGL((decode_qknorm_kernel<D, float>), grid, block, 0, s, a);
     else
         hipLaunchKernelGGL((decode_kernel<D, float>), grid, block, 0, s, a);
     return hipGetLastError();

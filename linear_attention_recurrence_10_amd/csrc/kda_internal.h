@@ -29,6 +29,8 @@ struct PrefillArgs {
     bool bf16;
     float scale;
     uint32_t epoch;          // launch tag of the value slices' pacing (set by the MFMA launcher)
+    bool qk_norm;            // q and k are used as x / max(||x||, eps) (per token and head)
+    float qk_eps2;           // eps^2 of that normalisation
 };
 
 struct DecodeArgs {
@@ -41,6 +43,8 @@ struct DecodeArgs {
     int D;
     bool bf16;
     float scale;
+    bool qk_norm;            // q and k are used as x / max(||x||, eps)
+    float qk_eps2;           // eps^2 of that normalisation
 };
 
 // The backward pass (kda_bwd.hip): gradients of every input given dO and dhT.
@@ -86,6 +90,14 @@ hipError_t launch_kcp_combine(const float *M, const float *Bs, const float *h0, 
 // x -> +inf gives g_min.
 __device__ __forceinline__ float gate_of_logit(float x, float g_min) {
     return g_min * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
+
+// The factor of the q/k normalisation x / max(||x||, eps) from the sum of
+// squares s = ||x||^2: 1 / max(||x||, eps) = rsqrt(max(s, eps^2)), with the
+// hardware reciprocal square root (about 1 ulp).  eps^2 is a normal fp32
+// number (the entry points keep eps in [1e-18, 1e18]), so the factor is finite.
+__device__ __forceinline__ float norm_factor(float sumsq, float eps2) {
+    return __builtin_amdgcn_rsqf(fmaxf(sumsq, eps2));
 }
 
 // bf16 (stored as raw 16-bit patterns) and fp32 element loads.

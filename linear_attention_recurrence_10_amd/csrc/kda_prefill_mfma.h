@@ -58,6 +58,22 @@
 //   16x16x16 (bf16_1k):  A[m = n][k = 4g + i],  B[k = 4g + i][col = n]
 //   16x16x32 (bf16):     A[m = n][k = 8g + j],  B[k = 8g + j][col = n]
 //   result:              C[row = 4g + i][col = n]
+// q/k normalisation (the NORM variants): with c_t = 1 / max(||k_t||, eps) and
+// d_t = 1 / max(||q_t||, eps) per token, the normalised operands are
+// diag(c) Kb, diag(c) Kh and diag(d) Qb, and the chunk form becomes
+//   A = diag(c) A0 diag(c), A0 = strict_lower(diag(beta) Kb Kh^T)
+//   U' = M' (V - diag(c) Kb S0),  M' = diag(c) (I + A)^-1 diag(beta)   (U' = diag(c) U)
+//   O = scale diag(d) (Y + P U')                 S = diag(e^gamma_C) (S0 + Kh^T U')
+// with Kb, Kh, Qb, P, Y those of the raw q and k: no operand is rescaled.
+// Since (I + D A0 D)^-1 = D^-1 (I + D^2 A0)^-1 D for D = diag(c),
+//   M' = (I + diag(c^2) A0)^-1 diag(c beta):
+// the solver scales row r of A0 by c_r^2 and starts column s at c_s beta_s,
+// so each lane needs only the c of its own row.  ||k_t||^2 is the diagonal
+// of Kb Kh^T (the decay factors cancel), which the solver sums anyway;
+// ||q_t||^2 is the diagonal of one more (exact, one-pass) bf16 product of the
+// raw q per k-side wave.  The state waves take c into the subtraction
+// V - c X (a fused multiply-add) and scale d into o's store.
+//
 // "Token per lane": lane (n, g) holds token n of the chunk and, in slot j of
 // an 8-wide operand of quarter kw, key channel 32 kw + 4g + j (j < 4) or
 // 32 kw + 16 + 4g + j - 4 (j >= 4).  This is the operand layout of every
@@ -263,6 +279,15 @@ struct Smem {
     f32x4 xy[2][2][2][64];        // partial X, Y [row half][X, Y][column tile][lane]
     uint32_t flag[2][2];          // state-wave handshake [column tile][row half]
 };
+// The q/k normalisation's LDS (after everything else, so the variants without
+// it keep their layout).
+struct NormLds {
+    float qq[kRing][4 * kKSW][kC];  // partial ||q_t||^2 [ring slot][k-side wave][token]
+    float f[kRing][2][kC];          // [ring slot][c, scale d][token], for the state waves
+};
+struct SmemNorm : Smem {
+    NormLds nrm;
+};
 
 // Pacing of the four value slices of one (b, h).  They run on four compute
 // units of one XCD and read the same q, k and g, so the XCD's L2 serves the
@@ -287,6 +312,7 @@ constexpr int kPaceSpin = 4096;
 // 2, the pacing to the one on SIMD 1.
 constexpr int kPSolver = 2;
 constexpr int kPaceSolver = 1;
+constexpr int kNormSolver = 1;  // forms the state waves' q/k normalisation factors
 __device__ uint64_t g_pace[kPaceSlots];
 
 // Reports of the slices of one (b, h): lane s < 4 reads slice s's entry.
@@ -475,6 +501,41 @@ __device__ __forceinline__ void kside_in(const PrefillArgs &a, const KRaw &raw, 
     }
 }
 
+// Component (n % 4) of x: in lane (n, g = n / 4) of a 16x16 product's result,
+// the diagonal element (n, n).  Three selects on lane-constant masks.
+__device__ __forceinline__ float diag_of(f32x4 x, int n16) {
+    const float lo = (n16 & 1) ? x[1] : x[0];
+    const float hi = (n16 & 1) ? x[3] : x[2];
+    return (n16 & 2) ? hi : lo;
+}
+// x summed over the four lanes n + 16 g of each n, with gfx950's cross-row
+// swaps: after v_permlane16_swap the two registers hold the values of lanes
+// l and l ^ 16, after v_permlane32_swap those of lanes l and l ^ 32.  (Written
+// out because the compiler folds the two results of the builtins' pair into
+// one when they are added; the s_nop gives the two wait states a swap needs
+// after a vector write of its operands, which the compiler cannot see here.)
+__device__ __forceinline__ float row_group_sum(float x) {
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    float c = a + b, d = c;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(c), "+v"(d));
+    return c + d;
+}
+// ||q_t||^2 over this k-side wave's channels: the diagonal of the raw q's Gram
+// (bf16 products are exact in fp32), one product on the loaded registers.
+__device__ __forceinline__ void kside_qq(float (&qq)[4 * kKSW][kC], const KRaw &raw, int kw, int grp, int n16) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 gq;
+    if constexpr (kKSW == 1) {
+        const bf16x8 qr = __builtin_bit_cast(bf16x8, u32x4{raw.q[0][0], raw.q[0][1], raw.q[1][0], raw.q[1][1]});
+        gq = mfma32(qr, qr, zero);
+    } else {
+        const bf16x4 qr = __builtin_bit_cast(bf16x4, raw.q[0]);
+        gq = mfma16(qr, qr, zero);
+    }
+    if (grp == (n16 >> 2)) qq[kw][n16] = diag_of(gq, n16);
+}
+
 // K-side, second part: this quarter's operands of the chunk go to `op` (LDS or
 // a shared slot in global memory), its partial Grams to `gr`, beta to `bt`.
 // Without QS (no o) neither Qb nor P is formed.
@@ -603,18 +664,40 @@ __device__ __forceinline__ void kside_tile(Ops &op, f32x4 (&gr)[4 * kKSW][2][64]
 
 // M = (I + A)^-1 diag(beta) and P of the chunk whose Grams sit in the `par`
 // buffers: solver wave kw solves columns 4 kw .. 4 kw + 3, one per 16-lane row.
-template <bool QS>
+// NORM: c comes from the diagonal of the summed Gram, ||q||^2 from the k-side
+// partials in nl->qq[slot]; row r of A is scaled by c_r^2 and column s starts
+// at c_s beta_s (which gives diag(c) M), and solver kNormSolver leaves c and
+// scale d in nl->f[slot].
+template <bool QS, bool NORM>
 __device__ __forceinline__ void solve(const f32x4 (&gr)[4 * kKSW][2][64], const float (&bt)[kC], f32x4 (&arow)[kC][5],
                                       bf16x4 (&Mo)[2][64], bf16x4 (&Po)[2][64], int kw, int grp, int n16,
-                                      int lane) {
+                                      int lane, NormLds *nl, int slot, float eps2, float scale) {
     // lane (row r = n, column group g): sum the partial Grams of row r, columns 4g .. 4g + 3
     f32x4 as = gr[0][0][lane];
 #pragma unroll
     for (int ww = 1; ww < 4 * kKSW; ++ww) as += gr[ww][0][lane];
     const float nbeta_r = -bt[n16];
     f32x4 av;  // row r of -A
+    float cr = 1.f;  // NORM: c of this lane's row
+    if constexpr (NORM) {
+        // (Kb Kh^T)[t][t] = ||k_t||^2 sits in lane (t, t / 4), component t % 4;
+        // the sum over the row groups brings it to every lane (t, g)
+        const bool dlane = grp == (n16 >> 2);
+        cr = norm_factor(row_group_sum(dlane ? diag_of(as, n16) : 0.f), eps2);
+        const float nbc = nbeta_r * (cr * cr);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) av[i] = (4 * grp + i < n16) ? nbeta_r * as[i] : 0.f;
+        for (int i = 0; i < 4; ++i) av[i] = (4 * grp + i < n16) ? nbc * as[i] : 0.f;
+        if (kw == kNormSolver && dlane) {
+            float sq = nl->qq[slot][0][n16];
+#pragma unroll
+            for (int ww = 1; ww < 4 * kKSW; ++ww) sq += nl->qq[slot][ww][n16];
+            nl->f[slot][0][n16] = cr;
+            nl->f[slot][1][n16] = scale * norm_factor(sq, eps2);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = (4 * grp + i < n16) ? nbeta_r * as[i] : 0.f;
+    }
     arow[n16][grp] = av;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -627,11 +710,11 @@ __device__ __forceinline__ void solve(const f32x4 (&gr)[4 * kKSW][2][64], const 
         for (int j = 0; j < 4; ++j) nar[4 * u4 + j] = row[j];
     }
     const int s = 4 * kw + grp;  // the column this lane solves
-    float x = (n16 == s) ? 1.f : 0.f;
+    float x = (n16 == s) ? (NORM ? bt[s] * cr : 1.f) : 0.f;  // NORM: c_s beta_s (cr = c_s in row s)
     tri_pivots<0>(x, nar);
     // M[n][s] goes to slot s % 4 = grp of lane 16 (s / 4) + n = 16 kw + n of
     // the A operand of U = M Z, as a hi/lo bf16 pair
-    const float m = x * bt[s];
+    const float m = NORM ? x : x * bt[s];
     const __bf16 mh = static_cast<__bf16>(m);
     const __bf16 ml = static_cast<__bf16>(m - static_cast<float>(mh));
     reinterpret_cast<__bf16 *>(&Mo[0][16 * kw + n16])[grp] = mh;
@@ -692,15 +775,22 @@ __device__ __forceinline__ float quad_bcast(float x) {
 // the state update S = diag(e^gamma_C) (S0 + Kh^T U) of this wave's rows.
 // `op` is chunk n's ring slot (M, P are read from it here; the rest is in
 // `cur`), `nx` chunk n + 1's, whose operands are read into `nxt`.
-template <int MODE>
+// NORM: nf holds the chunk's normalisation factors (c and scale d of token t
+// in nf[0][t], nf[1][t]); M arrives as diag(c) M.
+template <int MODE, bool NORM>
 __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, const Ops &op, const Ops &nx, int64_t n,
                                             const SeqBase &sb, const Geom &gm, f32x4 (&S)[4], bf16x8 (&Shi)[2],
                                             const SOps &cur, SOps &nxt, int rh, int ct, int grp, int n16, int lane,
-                                            uint32_t ob0, uint32_t so, bf16x4 ident) {
+                                            uint32_t ob0, uint32_t so, bf16x4 ident, const float (*nf)[kC]) {
     constexpr bool QS = MODE == kFull;  // Y and O only where o is written
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const Sp4 Mf = Sp4{op.Mhl[0][lane], op.Mhl[1][lane]};
     const Sp4 Pf = Sp4{op.P[0][lane], op.P[1][lane]};
+    f32x4 ck = zero, osc = zero;  // NORM: c and scale d of tokens 4g + i
+    if constexpr (NORM) {
+        ck = *reinterpret_cast<const f32x4 *>(&nf[0][4 * grp]);
+        osc = *reinterpret_cast<const f32x4 *>(&nf[1][4 * grp]);
+    }
     // this chunk's values are read with M and P, ahead of the handshake: LDS
     // reads complete in order, so a read issued after the handshake would
     // also wait for the next chunk's operand reads issued there
@@ -759,7 +849,10 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
         vv[2] = __uint_as_float(vp[1] << 16);
         vv[3] = __uint_as_float(vp[1] & 0xffff0000u);
     }
-    const Sp4 U = split4(mm16(Mf, split4(vv - X), zero));
+    // NORM: V - diag(c) Kb S0, and M = diag(c) M gives U' = diag(c) U, which
+    // the update and P U' then take with the raw Kh and P
+    const f32x4 Z = NORM ? vv - ck * X : vv - X;
+    const Sp4 U = split4(mm16(Mf, split4(Z), zero));
 
     if (owave && MODE == kFull) {
         const f32x4 O = mm16(Pf, U, Y + Yo);
@@ -767,7 +860,8 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs &a, Smem &sm, cons
         const Rsrc ro = chunk_rsrc<kD, 4>(sb.o, gm, static_cast<int>(n));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, a.scale * O[i]), ro, ob0, i * so, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, (NORM ? osc[i] : a.scale) * O[i]), ro,
+                                                  ob0, i * so, 0);
     }
 
     // S: lane (n, g) holds rows 4g + i of tile t, channel 64 rh + 16 t + 4 g + i,
@@ -854,11 +948,13 @@ __device__ __forceinline__ void run_steps(int64_t nchunks, Body &&body) {
     }
 }
 
-// CKPT: the launch writes state checkpoints (a separate instantiation, so the
-// plain prefill carries no test for it).  MODE: a PassMode.
-template <bool CKPT, int G, int MODE>  // G: GateMode
-__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
-    __shared__ Smem sm;
+// The kernel body.  CKPT: the launch writes state checkpoints (a separate
+// instantiation, so the plain prefill carries no test for it).  MODE: a
+// PassMode.  NORM: q and k are normalised (with kFull only).
+template <bool CKPT, int G, int MODE, bool NORM>  // G: GateMode
+__device__ __forceinline__ void prefill_mfma_body(PrefillArgs a) {
+    static_assert(!NORM || MODE == kFull, "the q/k normalisation comes with the full prefill only");
+    __shared__ std::conditional_t<NORM, SmemNorm, Smem> sm;
     constexpr bool QS = MODE == kFull;  // q, Qb, P and Y are needed only where o is written
 
     const int tid = threadIdx.x;
@@ -941,6 +1037,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             KIn in;
             if constexpr (decltype(kside_tag)::value) kside_in<G, QS>(a, raw[PAR], in, static_cast<int>(n) + 2, gm, n16);
             if constexpr (decltype(kside_tag)::value) {
+                if constexpr (NORM) kside_qq(sm.nrm.qq[kslot], raw[PAR], kw, grp, n16);
                 if constexpr (kKSW == 1)
                     kside<QS>(sm.ops[kslot], sm.gram[PAR], sm.beta[PAR], in, kw, grp, n16, lane);
                 else
@@ -977,8 +1074,10 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
                     rep = pace_read(pace_e, lane);
                 }
                 if constexpr (MODE != kNoValue) v2 = load_v2(sb, gm, min(static_cast<int>(n) + 2, nlast), vb0);
-                solve<QS>(sm.gram[PAR ^ 1], sm.beta[PAR ^ 1], sm.arow[sv], sm.ops[vslot].Mhl, sm.ops[vslot].P, sv, grp,
-                      n16, lane);
+                NormLds *nl = nullptr;
+                if constexpr (NORM) nl = &sm.nrm;
+                solve<QS, NORM>(sm.gram[PAR ^ 1], sm.beta[PAR ^ 1], sm.arow[sv], sm.ops[vslot].Mhl, sm.ops[vslot].P,
+                                sv, grp, n16, lane, nl, vslot, a.qk_eps2, a.scale);
             }
             vslot = (vslot == kRing - 1) ? 0 : vslot + 1;
         });
@@ -998,8 +1097,10 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             constexpr int PAR = decltype(par_tag)::value;
             const int nslot = (sslot == kRing - 1) ? 0 : sslot + 1;  // chunk n + 1
             if constexpr (decltype(state_tag)::value) {
-                state_chunk<MODE>(a, sm, sm.ops[sslot], sm.ops[nslot], n, sb, gm, S, Shi, so[PAR], so[PAR ^ 1], rh, ct,
-                                  grp, n16, lane, 4u * voff0, 4u * HD, ident);
+                const float(*nf)[kC] = nullptr;
+                if constexpr (NORM) nf = sm.nrm.f[sslot];
+                state_chunk<MODE, NORM>(a, sm, sm.ops[sslot], sm.ops[nslot], n, sb, gm, S, Shi, so[PAR], so[PAR ^ 1],
+                                        rh, ct, grp, n16, lane, 4u * voff0, 4u * HD, ident, nf);
                 if (CKPT && --ck_left == 0) {  // the state after (ck_i + 1) * ckpt_every chunks
                     if (ck_i < a.n_ckpt) {
                         float *ck = a.ckpt + ck_i * (BH * kD * kD) + sbase;
@@ -1032,6 +1133,17 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
             }
         }
     }
+}
+
+template <bool CKPT, int G, int MODE>  // G: GateMode
+__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
+    prefill_mfma_body<CKPT, G, MODE, false>(a);
+}
+// The prefill with the q/k normalisation (a kernel of its own name, so that
+// kernel traces tell it from the plain one).
+template <int G>  // GateMode
+__global__ __launch_bounds__(kThreads) void prefill_mfma_qknorm_kernel(PrefillArgs a) {
+    prefill_mfma_body<false, G, kFull, true>(a);
 }
 
 }  // namespace

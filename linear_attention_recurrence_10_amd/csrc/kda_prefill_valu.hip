@@ -19,6 +19,9 @@
 // lower-triangular system above.  The chunk length 16 with gates >= -5 keeps
 // e^(+-gamma) inside the normal fp32/bf16 range (Kimi K3 paper digest,
 // devpress.csdn.net, section 2.1 (1)).
+//
+// With the q/k normalisation on, each staged q and k row is scaled by
+// 1 / max(||x||, eps) before anything else reads it.
 #include "kda_internal.h"
 
 namespace kda {
@@ -43,6 +46,7 @@ __global__ __launch_bounds__(DVS *RG) void prefill_valu_kernel(PrefillArgs a) {
     __shared__ float sP[C][C + 1];
     __shared__ float sBeta[C];
     __shared__ float sGC[D];  // e^gamma_C
+    __shared__ float sNrm[2 * C];  // q/k normalisation factors [q rows, k rows]
 
     const int tid = threadIdx.x;
     const int c = tid / RG;   // value column inside the slice
@@ -102,6 +106,24 @@ __global__ __launch_bounds__(DVS *RG) void prefill_valu_kernel(PrefillArgs a) {
             sBeta[tid] = (t < T) ? a.beta[(b * T + t) * H + h] : 0.f;
         }
         __syncthreads();
+
+        // (1b) q/k normalisation (work-group uniform branch): one thread per
+        //      row sums its squares, then every element is scaled
+        if (a.qk_norm) {
+            for (int rr = tid; rr < 2 * C; rr += NT) {
+                const float *row = rr < C ? sQ[rr] : sKh[rr - C];
+                float ss = 0.f;
+                for (int i = 0; i < D; ++i) ss += row[i] * row[i];
+                sNrm[rr] = norm_factor(ss, a.qk_eps2);
+            }
+            __syncthreads();
+            for (int e = tid; e < C * D; e += NT) {
+                const int r = e / D, i = e % D;
+                sQ[r][i] *= sNrm[r];
+                sKh[r][i] *= sNrm[C + r];
+            }
+            __syncthreads();
+        }
 
         // (2) per-channel cumulative log-decay and the decay-scaled operands
         for (int i = tid; i < D; i += NT) {

@@ -178,6 +178,49 @@ def test_gate_shares_the_prefill_checks(lib):
     assert b"o overlaps g" in lib.kda_last_error()
 
 
+# ---- the q/k normalisation (kda_chunk_fwd_qknorm, kda_decode_step_qknorm) ----
+
+def chunk_qknorm(lib, gate=0, g_min=-5.0, eps=1e-12, T=64, ptrs=None):
+    p = ptrs or [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(8)]
+    return lib.kda_chunk_fwd_qknorm(p[0], p[1], p[2], p[3], gate, g_min, eps, p[4], p[5], p[6], p[7],
+                                    1, T, 1, 128, 128, 1, 0.0, None)
+
+
+@pytest.mark.parametrize("eps", [0.0, -1.0, 1e-19, 1e19, float("nan"), float("inf")])
+def test_qknorm_eps_out_of_range(lib, eps):
+    assert chunk_qknorm(lib, eps=eps) == 1
+    assert b"eps" in lib.kda_last_error()
+    p = [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(7)]
+    assert lib.kda_decode_step_qknorm(*p, 1, 1, 128, 128, 1, 0.0, eps, None) == 1
+    assert b"eps" in lib.kda_last_error()
+
+
+def test_qknorm_gate_kind_and_floor(lib):
+    assert chunk_qknorm(lib, gate=3) == 1
+    assert b"gate kind" in lib.kda_last_error()
+    assert chunk_qknorm(lib, gate=2, g_min=0.5) == 1
+    assert b"g_min" in lib.kda_last_error()
+    # with the log-decay gate g_min is not used: the call gets past the argument
+    # checks (to the overlap check planted here)
+    ptrs = [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(8)]
+    ptrs[6] = ctypes.c_void_p(ptrs[3].value + 64)   # o inside g
+    assert chunk_qknorm(lib, gate=0, g_min=7.0, ptrs=ptrs) == 1
+    assert b"o overlaps g" in lib.kda_last_error()
+
+
+def test_qknorm_shares_the_prefill_checks(lib):
+    assert chunk_qknorm(lib, T=-1) == 1
+    ptrs = [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(8)]
+    ptrs[0] = None
+    assert chunk_qknorm(lib, ptrs=ptrs) == 1
+    assert b"non-null" in lib.kda_last_error()
+    p = [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(7)]
+    assert lib.kda_decode_step_qknorm(*p, 0, 1, 128, 128, 1, 0.0, 1e-6, None) == 1
+    p[6] = ctypes.c_void_p(p[5].value + 64)          # o inside the state
+    assert lib.kda_decode_step_qknorm(*p, 1, 1, 128, 128, 1, 0.0, 1e-6, None) == 1
+    assert b"overlaps" in lib.kda_last_error()
+
+
 # ---- the segmented prefill (kda_chunk_fwd_kcp) ----
 
 def chunk_kcp(lib, n_seg=4, T=64, ws=0x7000000, ws_bytes=1 << 30, B=1, H=1, D=128):
