@@ -520,6 +520,629 @@ __global__ __launch_bounds__(512) void bwd_col_kernel(BwdArgs a) {
     }
 }
 
+// ---- The chunk-form adjoint on the fp32 matrix cores (d = 128) ----
+//
+// The forward pass over a 16-token chunk with start state S0 (rows = key
+// channels), per-channel cumulative log-decay gamma and D_C = diag(e^gamma_C):
+//   Qb = q e^gamma, Kb = k e^gamma, Kh = k e^-gamma
+//   A = strict_lower(diag(beta) Kb Kh^T),  N = (I + A)^-1,  M = N diag(beta)
+//   P = lower(Qb Kh^T),  Z = V - Kb S0,  U = M Z
+//   O = scale (Qb S0 + P U),  S = D_C (S0 + Kh^T U)
+// is an exact regrouping of the token recurrence, so its adjoint is the
+// gradient.  Given dS = dL/dS and the chunk's dO, with G = D_C dS:
+//   dU = Kh G + scale P^T dO,  dZ = M^T dU  (= dv),  dM = dU Z^T,  dP = scale dO U^T
+//   dS0 = G - Kb^T dZ + scale Qb^T dO                  (the next dS, one chunk back)
+//   dN = dM diag(beta),  dA = -N^T dN N^T,  dGr = diag(beta) strict_lower(dA)
+//   dbeta_s = sum_r dM_rs N_rs + sum_(u < s) dA_su (Kb Kh^T)_su
+//   dQb = scale dO S0^T + dP Kh,  dKb = -dZ S0^T + dGr Kh,  dKh = U G^T + dGr^T Kb + dP^T Qb
+//   dq = dQb e^gamma,  dk = dKb e^gamma + dKh e^-gamma
+//   dgamma = dQb Qb + dKb Kb - dKh Kh,  plus rowsum(S .* dS) on gamma_C
+//   dg_t = sum over u >= t of dgamma_u, plus the gamma_C term (every token of the chunk)
+// In that last sum the pairs of tokens inside the chunk cancel except where
+// they straddle t.  The pair of the state update (D_C Kh^T U, whose factor is
+// e^(gamma_C - gamma_s)) is taken out of the cancellation: with W = (U G^T) .* Kh,
+//   dg_t = sum_(u >= t) (dgamma_u + W_u) + rowsum(S0 .* G) + sum_(s < t) W_s,
+// and so is the diagonal of P, whose pair has no decay factor at all: the
+// products take dP without its diagonal, and the diagonal adds dP_tt k_t to
+// dq_t and dP_tt q_t to dk_t directly.
+// One work-group per (b, h, 32-column slice), four waves.  The columns of S
+// and dS are independent, so dS0, dZ and the slice's dv and dh0 are exact per
+// slice; everything that sums over columns (dM, dP, the three d?b products
+// and the gamma_C term) is linear in this slice's part, so each slice forms
+// its share of dq, dk, dg and dbeta, and a second kernel sums the slices in a
+// fixed order.  Every product is a 16 x 16 output tile of fp32 matrix-core
+// instructions (16x16x4) with operands read from LDS; the phases of a chunk
+// are separated by work-group barriers.
+
+using f32x4 = float __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma4(float x, float y, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c, 0, 0, 0);
+}
+
+// c + A B for one 16 x 16 tile over K (a multiple of 4), A(r, k) =
+// pa[r sar + k sak] and B(k, j) = pb[k sbk + j sbc].  Lane l supplies A(l % 16,
+// k0 + l / 16) and B(k0 + l / 16, l % 16) to each step; component i of the
+// result is C(4 (l / 16) + i, l % 16).
+template <int K>
+__device__ __forceinline__ f32x4 tile_mm(const float *pa, int sar, int sak, const float *pb, int sbk, int sbc, f32x4 c,
+                                         int lane) {
+    const int r = lane & 15, kq = lane >> 4;
+    float av[K / 4], bv[K / 4];  // every operand is read before the first product
+#pragma unroll
+    for (int m = 0; m < K / 4; ++m) {
+        av[m] = pa[r * sar + (4 * m + kq) * sak];
+        bv[m] = pb[(4 * m + kq) * sbk + r * sbc];
+    }
+#pragma unroll
+    for (int m = 0; m < K / 4; ++m) c = mfma4(av[m], bv[m], c);
+    return c;
+}
+// The same where both operands are contiguous in k: A(r, k) = pa[r sa + k],
+// B(k, j) = pb[j sb + k] (rows 16-byte aligned, K a multiple of 16).  The
+// sum over k is taken in another order: in block kb of 16, lane group
+// kq = l / 16 supplies k = 16 kb + 4 kq + m to step m, so each lane reads
+// its four k of A and of B with one 16-byte load each.
+template <int K>
+__device__ __forceinline__ f32x4 tile_mm_kc(const float *pa, int sa, const float *pb, int sb, f32x4 c, int lane) {
+    const int r = lane & 15, kq = lane >> 4;
+    f32x4 av[K / 16], bv[K / 16];
+#pragma unroll
+    for (int kb = 0; kb < K / 16; ++kb) {
+        av[kb] = *reinterpret_cast<const f32x4 *>(pa + r * sa + 16 * kb + 4 * kq);
+        bv[kb] = *reinterpret_cast<const f32x4 *>(pb + r * sb + 16 * kb + 4 * kq);
+    }
+#pragma unroll
+    for (int kb = 0; kb < K / 16; ++kb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) c = mfma4(av[kb][m], bv[kb][m], c);
+    return c;
+}
+
+// the sum of x over the 16 lanes of each row, in every lane of the row
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp_mv<0xb1>(x);   // lane ^ 1
+    x += dpp_mv<0x4e>(x);   // lane ^ 2
+    x += dpp_mv<0x141>(x);  // the other quad of the 8
+    x += dpp_mv<0x140>(x);  // the other 8 of the row
+    return x;
+}
+
+// Forward substitution for one column of (I + A)^-1: lane (r, g) holds x_r of
+// the column its row group solves, nar row r of -A.  At pivot u every row
+// adds nar[u] times x_u, read from lane u of the same 16-lane row
+// (row_newbcast); A is strictly lower triangular, so rows r <= u keep their
+// value.
+template <int U>
+__device__ __forceinline__ void bwd_pivots(float &x, const float (&nar)[16]) {
+    if constexpr (U < 15) {
+        x += nar[U] * dpp_mv<0x150 + U>(x);
+        bwd_pivots<U + 1>(x, nar);
+    }
+}
+
+// The inputs of one chunk for thread tid, in registers: token t = tid / 16,
+// channels 8 p .. 8 p + 7 (p = tid % 16) of q, k (bf16) and g; v of the slice
+// (token (tid % 64) / 4, columns 8 (tid % 4) ..); dO of the slice (with
+// d = (tid - 64) % 128: token d / 8, columns 4 (d % 8) ..); the state before
+// the chunk, rows tid / 8 + 32 m, columns 4 (tid % 8) ..; beta of token
+// tid % 16.
+struct ChunkIn {
+    uint4 q, k, v;
+    float4 g0, g1, dO, s00, s01, s02, s03;
+    float beta;
+};
+
+// Global accesses of the chunk kernel go through buffer descriptors: a
+// wave-uniform base (token t0 of this (b, h)) with the number of bytes up to
+// the end of the chunk's last valid token, plus a 32-bit offset per lane.
+// Accesses of tokens past the end fall outside the range: loads return zeros
+// and stores are dropped, so no lane needs a test or a branch (and the
+// compiler can count the outstanding memory operations exactly).  The
+// launcher keeps 16 H D 4 below 2^31.
+using Rsrc = __amdgpu_buffer_rsrc_t;
+using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ Rsrc buf(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                            0x00020000);
+}
+__device__ __forceinline__ uint4 ld16(Rsrc r, uint32_t off) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ float4 ld16f(Rsrc r, uint32_t off) {
+    const uint4 x = ld16(r, off);
+    return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w));
+}
+__device__ __forceinline__ void st4(Rsrc r, uint32_t off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+}
+
+// tok0: row of token t0 of this (b, h) in [B, T, H] rows; nt: valid tokens
+// of the chunk; s0: the state before the chunk (null: zero).
+__device__ __forceinline__ ChunkIn load_chunk_inputs(const BwdArgs &a, int64_t tok0, int nt, int col0,
+                                                     const float *s0, int64_t sb, int tid) {
+    constexpr int D = 128;
+    const uint32_t H = static_cast<uint32_t>(a.H), HD = H * D, last = static_cast<uint32_t>(nt - 1) * HD;
+    const int t = tid >> 4, p = tid & 15;
+    const uint32_t off = static_cast<uint32_t>(t) * HD + 8 * p;  // elements
+    const Rsrc rq = buf(static_cast<const uint16_t *>(a.q) + tok0 * D, 2 * (last + D));
+    const Rsrc rk = buf(static_cast<const uint16_t *>(a.k) + tok0 * D, 2 * (last + D));
+    const Rsrc rg = buf(a.g + tok0 * D, 4 * (last + D));
+    const Rsrc rv = buf(static_cast<const uint16_t *>(a.v) + tok0 * D + col0, 2 * (last + 32));
+    const Rsrc rd = buf(a.dO + tok0 * D + col0, 4 * (last + 32));
+    const Rsrc rs = buf(s0 ? s0 + sb + col0 : nullptr, s0 ? 4u * (127 * D + 32) : 0u);
+    const Rsrc rb = buf(a.beta + tok0, 4 * (static_cast<uint32_t>(nt - 1) * H + 1));
+    ChunkIn in;
+    in.q = ld16(rq, 2 * off);
+    in.k = ld16(rk, 2 * off);
+    in.g0 = ld16f(rg, 4 * off);
+    in.g1 = ld16f(rg, 4 * off + 16);
+    // (v is stored by threads 0..63 and dO by threads 64..191, each thread the
+    // piece it loads; the others load a piece too, to keep the loads free of
+    // branches)
+    const int l = tid & 63, l2 = (tid - 64) & 127;
+    in.v = ld16(rv, 2 * (static_cast<uint32_t>(l >> 2) * HD + 8 * (l & 3)));
+    in.dO = ld16f(rd, 4 * (static_cast<uint32_t>(l2 >> 3) * HD + 4 * (l2 & 7)));
+    const uint32_t so = 4 * (static_cast<uint32_t>(tid >> 3) * D + 4 * (tid & 7));
+    in.s00 = ld16f(rs, so);
+    in.s01 = ld16f(rs, so + 4 * 32 * D);
+    in.s02 = ld16f(rs, so + 4 * 64 * D);
+    in.s03 = ld16f(rs, so + 4 * 96 * D);
+    in.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, 4 * (static_cast<uint32_t>(tid & 15) * H), 0, 0));
+    return in;
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int P, int PS>
+__device__ __forceinline__ void put_row4(float (*sS0)[PS], float (*sS0T)[P], int c, int j, float4 x) {
+    sS0[c][j] = x.x;
+    sS0[c][j + 1] = x.y;
+    sS0[c][j + 2] = x.z;
+    sS0[c][j + 3] = x.w;
+    sS0T[j][c] = x.x;
+    sS0T[j + 1][c] = x.y;
+    sS0T[j + 2][c] = x.z;
+    sS0T[j + 3][c] = x.w;
+}
+
+template <int P, int PS>
+__device__ __forceinline__ void store_chunk_inputs(const ChunkIn &in, int nt, int tid, float (*sQ)[P], float (*sK)[P],
+                                                   float (*sG)[P], float (*sV)[PS], float (*sDO)[PS], float (*sS0)[PS],
+                                                   float (*sS0T)[P], float *sBeta) {
+    const int t = tid >> 4, c = 8 * (tid & 15);
+    const bool live = t < nt;
+    sQ[t][c + 0] = live ? bf_lo(in.q.x) : 0.f;
+    sQ[t][c + 1] = live ? bf_hi(in.q.x) : 0.f;
+    sQ[t][c + 2] = live ? bf_lo(in.q.y) : 0.f;
+    sQ[t][c + 3] = live ? bf_hi(in.q.y) : 0.f;
+    sQ[t][c + 4] = live ? bf_lo(in.q.z) : 0.f;
+    sQ[t][c + 5] = live ? bf_hi(in.q.z) : 0.f;
+    sQ[t][c + 6] = live ? bf_lo(in.q.w) : 0.f;
+    sQ[t][c + 7] = live ? bf_hi(in.q.w) : 0.f;
+    sK[t][c + 0] = live ? bf_lo(in.k.x) : 0.f;
+    sK[t][c + 1] = live ? bf_hi(in.k.x) : 0.f;
+    sK[t][c + 2] = live ? bf_lo(in.k.y) : 0.f;
+    sK[t][c + 3] = live ? bf_hi(in.k.y) : 0.f;
+    sK[t][c + 4] = live ? bf_lo(in.k.z) : 0.f;
+    sK[t][c + 5] = live ? bf_hi(in.k.z) : 0.f;
+    sK[t][c + 6] = live ? bf_lo(in.k.w) : 0.f;
+    sK[t][c + 7] = live ? bf_hi(in.k.w) : 0.f;
+    sG[t][c + 0] = live ? in.g0.x : 0.f;
+    sG[t][c + 1] = live ? in.g0.y : 0.f;
+    sG[t][c + 2] = live ? in.g0.z : 0.f;
+    sG[t][c + 3] = live ? in.g0.w : 0.f;
+    sG[t][c + 4] = live ? in.g1.x : 0.f;
+    sG[t][c + 5] = live ? in.g1.y : 0.f;
+    sG[t][c + 6] = live ? in.g1.z : 0.f;
+    sG[t][c + 7] = live ? in.g1.w : 0.f;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (wv == 0) {
+        const int vt = tid >> 2, vc = 8 * (tid & 3);
+        const bool vl = vt < nt;
+        sV[vt][vc + 0] = vl ? bf_lo(in.v.x) : 0.f;
+        sV[vt][vc + 1] = vl ? bf_hi(in.v.x) : 0.f;
+        sV[vt][vc + 2] = vl ? bf_lo(in.v.y) : 0.f;
+        sV[vt][vc + 3] = vl ? bf_hi(in.v.y) : 0.f;
+        sV[vt][vc + 4] = vl ? bf_lo(in.v.z) : 0.f;
+        sV[vt][vc + 5] = vl ? bf_hi(in.v.z) : 0.f;
+        sV[vt][vc + 6] = vl ? bf_lo(in.v.w) : 0.f;
+        sV[vt][vc + 7] = vl ? bf_hi(in.v.w) : 0.f;
+    } else if (wv < 3) {
+        const int dt = (tid - 64) >> 3, dc = 4 * ((tid - 64) & 7);
+        const bool dl = dt < nt;
+        sDO[dt][dc] = dl ? in.dO.x : 0.f;
+        sDO[dt][dc + 1] = dl ? in.dO.y : 0.f;
+        sDO[dt][dc + 2] = dl ? in.dO.z : 0.f;
+        sDO[dt][dc + 3] = dl ? in.dO.w : 0.f;
+    }
+    const int r0 = tid >> 3, j = 4 * (tid & 7);
+    put_row4(sS0, sS0T, r0, j, in.s00);
+    put_row4(sS0, sS0T, r0 + 32, j, in.s01);
+    put_row4(sS0, sS0T, r0 + 64, j, in.s02);
+    put_row4(sS0, sS0T, r0 + 96, j, in.s03);
+    if (tid < 16) sBeta[tid] = tid < nt ? in.beta : 0.f;
+}
+
+// A work-group barrier that orders LDS only: the waves' LDS writes are complete
+// and visible after it, while their global loads (the next chunk's inputs)
+// and stores (this chunk's outputs) stay in flight across it.  (A full
+// barrier is a workgroup-scope fence, which on this target waits for every
+// outstanding global access.)
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// bf16 inputs (fp32 inputs take the token-serial kernel).
+__global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
+    constexpr int D = 128, kCW = 32, kNS = D / kCW, kC = 16;
+    constexpr int kP = 132;  // pitch of the token x channel arrays
+    constexpr int kPS = 36;  // pitch of the channel x column and token x column arrays
+    constexpr int kP16 = 20; // pitch of the 16 x 16 arrays
+    __shared__ float sQb[kC][kP], sKb[kC][kP], sKh[kC][kP], sEg[kC][kP], sEgi[kC][kP], sDgam[kC][kP], sW[kC][kP];
+    __shared__ float sS0[D][kPS], sG[D][kPS];
+    __shared__ float sS0T[kCW][kP], sGT[kCW][kP];  // transposed copies: column j, channel c
+    __shared__ float sV[kC][kPS], sDO[kC][kPS], sZ[kC][kPS], sU[kC][kPS], sdU[2][kC][kPS], sdZ[kC][kPS];
+    __shared__ float sA[kC][kP16], sGr[kC][kP16], sPs[kC][kP16], sN[kC][kP16], sM[kC][kP16];
+    __shared__ float sdM[kC][kP16], sdP[kC][kP16], sdGr[kC][kP16], sT1[kC][kP16];
+    __shared__ float sBeta[kC], sDgC[D], sDB[kC], sDPd[kC];
+
+    const int64_t bh = blockIdx.x / kNS;
+    const int slice = static_cast<int>(blockIdx.x % kNS);
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const int tid_k = threadIdx.x, tid = tid_k, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid_k >> 6);  // wave-uniform: its branches and offsets are scalar
+    const int64_t T = a.T, H = a.H;
+    const int col0 = slice * kCW;
+    float *part = a.part + static_cast<int64_t>(slice) * a.part_stride;
+    const int64_t BHD = a.B * a.H * D * D;
+    const int64_t sb = bh * D * D;
+    const uint32_t HD = static_cast<uint32_t>(a.H) * D;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    // dS, this wave's four tiles of the 128 x 32 slice: tile q is row block
+    // 2 w + q / 2, column tile q % 2; component i is row 4 g4 + i of the block
+    f32x4 dS[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int rb = 2 * w + (q >> 1), ct = q & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dS[q][i] = a.dhT ? a.dhT[sb + (16 * rb + 4 * g4 + i) * D + col0 + 16 * ct + r16] : 0.f;
+    }
+
+    const int64_t nch = (T + kC - 1) / kC;
+    ChunkIn in{};
+    if (nch > 0) {
+        const int64_t t0 = (nch - 1) * kC;
+        in = load_chunk_inputs(a, (b * T + t0) * H + h, static_cast<int>(T - t0), col0,
+                               nch - 1 == 0 ? a.h0 : a.ckpt + (nch - 2) * BHD, sb, tid);  // (the last chunk)
+    }
+    for (int64_t n = nch - 1; n >= 0; --n) {
+        const int64_t t0 = n * kC;
+        const int nt = static_cast<int>(t0 + kC < T ? kC : T - t0);
+        // The lane's indices, made opaque to the compiler once per chunk: the
+        // LDS addresses of the chunk are then formed in the loop from a few
+        // registers instead of being kept, one register each, across it.
+        int tidv = tid_k;
+        asm volatile("" : "+v"(tidv));
+        const int tid = tidv, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+        // this chunk's outputs: wave-uniform bases at token t0 plus 32-bit lane offsets
+        const int64_t tok0 = (b * T + t0) * H + h;
+        const uint32_t last = static_cast<uint32_t>(nt - 1) * HD;
+        const Rsrc dvb = buf(a.dv + tok0 * D + col0, 4 * (last + 32));
+        const Rsrc pq = buf(part + tok0 * D, 4 * (last + D));
+        const Rsrc pk = buf(part + a.part_plane + tok0 * D, 4 * (last + D));
+        const Rsrc pg = buf(part + 2 * a.part_plane + tok0 * D, 4 * (last + D));
+        const Rsrc pb = buf(part + 3 * a.part_plane + tok0, 4 * (static_cast<uint32_t>(nt - 1) * static_cast<uint32_t>(H) + 1));
+        lds_barrier();  // the previous chunk is done with LDS
+
+        // (L) the chunk's inputs, loaded during the previous chunk (or before
+        //     the loop), to LDS: q, k and g land in sQb, sKb and sKh, which the
+        //     pass after the barrier turns into Qb, Kb, Kh
+        store_chunk_inputs(in, nt, tid, sQb, sKb, sKh, sV, sDO, sS0, sS0T, sBeta);
+        lds_barrier();
+        // the next chunk's loads are in flight while this one is worked on
+        // (in the last step, chunk 0 again: the loads are the same every step)
+        {
+            const int64_t np = n > 0 ? n - 1 : 0;
+            in = load_chunk_inputs(a, (b * T + np * kC) * H + h, n > 0 ? kC : nt, col0,
+                                   np == 0 ? a.h0 : a.ckpt + (np - 1) * BHD, sb, tid);
+        }
+        // the cumulative log-decay, in place of g (a thread per channel) ...
+        if (tid < D) {
+            float gv[kC];
+#pragma unroll
+            for (int t = 0; t < kC; ++t) gv[t] = sKh[t][tid];
+            float gam = 0.f;
+#pragma unroll
+            for (int t = 0; t < kC; ++t) {
+                gam += gv[t];
+                sKh[t][tid] = gam;
+            }
+        }
+        lds_barrier();
+        // ... then the decay factors and the scaled operands, thread (t = tid /
+        // 16, channels 8 (tid % 16) ..); e^gamma_C is row 15 of sEg
+        {
+            const int t = tid >> 4, c0 = 8 * (tid & 15);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = c0 + j;
+                const float gam = sKh[t][c], qv = sQb[t][c], kv = sKb[t][c];
+                const float e = __expf(gam), ei = __expf(-gam);
+                sQb[t][c] = qv * e;
+                sKb[t][c] = kv * e;
+                sKh[t][c] = kv * ei;
+                sEg[t][c] = e;
+                sEgi[t][c] = ei;
+            }
+        }
+        lds_barrier();
+
+        // (F1) Kb Kh^T and A (wave 0), scale P (wave 1), Z = V - Kb S0 (waves 2, 3)
+        if (w == 0) {
+            const f32x4 gr = tile_mm_kc<D>(&sKb[0][0], kP, &sKh[0][0], kP, zero, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * g4 + i;
+                sGr[r][r16] = gr[i];
+                sA[r][r16] = r16 < r ? sBeta[r] * gr[i] : 0.f;
+            }
+        } else if (w == 1) {
+            const f32x4 pr = tile_mm_kc<D>(&sQb[0][0], kP, &sKh[0][0], kP, zero, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * g4 + i;
+                sPs[r][r16] = r16 <= r ? a.scale * pr[i] : 0.f;
+            }
+        } else {
+            const int ct = w - 2;
+            const f32x4 x = tile_mm_kc<D>(&sKb[0][0], kP, &sS0T[16 * ct][0], kP, zero, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * g4 + i;
+                sZ[t][16 * ct + r16] = sV[t][16 * ct + r16] - x[i];
+            }
+        }
+        lds_barrier();
+
+        // (F2) N = (I + A)^-1 and M = N diag(beta): row group g4 of wave w solves column 4 w + g4
+        {
+            float nar[kC];
+#pragma unroll
+            for (int u = 0; u < kC; ++u) nar[u] = -sA[r16][u];
+            const int s = 4 * w + g4;
+            float x = r16 == s ? 1.f : 0.f;
+            bwd_pivots<0>(x, nar);
+            sN[r16][s] = x;
+            sM[r16][s] = x * sBeta[s];
+        }
+        lds_barrier();
+
+        // (F3) U = M Z (waves 0, 1); every wave starts its dQb tiles: dO S0^T
+        // (this wave's channel blocks cb = 2 w + e)
+        if (w < 2) {
+            const f32x4 uu = tile_mm<kC>(&sM[0][0], kP16, 1, &sZ[0][16 * w], kPS, 1, zero, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sU[4 * g4 + i][16 * w + r16] = uu[i];
+        }
+        f32x4 accQ[2], accKb[2], accKh[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            accQ[e] = tile_mm_kc<kCW>(&sDO[0][0], kPS, &sS0[16 * (2 * w + e)][0], kPS, zero, lane);
+
+        // (F4) G = D_C dS (kept in dS and written for the products) and the
+        // gamma_C term of D_C S0: rowsum(S0 .* G)
+        {
+            float dgc[2][4];
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dgc[e][i] = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int rb = 2 * w + (q >> 1), ct = q & 1;
+                f32x4 s0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s0[i] = sS0[16 * rb + 4 * g4 + i][16 * ct + r16];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * rb + 4 * g4 + i;
+                    dS[q][i] *= sEg[kC - 1][row];
+                    dgc[q >> 1][i] += s0[i] * dS[q][i];
+                    sG[row][16 * ct + r16] = dS[q][i];
+                    sGT[16 * ct + r16][row] = dS[q][i];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = row_sum16(dgc[e][i]);
+                    if (r16 == 0) sDgC[16 * (2 * w + e) + 4 * g4 + i] = v;
+                }
+        }
+        lds_barrier();
+
+        // (B1) dU = Kh G + scale P^T dO in two channel halves (wave w: column
+        // tile w % 2, half w / 2); dKh starts as U G^T; wave 3 forms dP
+        {
+            const int ct = w & 1, kh = w >> 1;
+            f32x4 du = tile_mm_kc<64>(&sKh[0][64 * kh], kP, &sGT[16 * ct][64 * kh], kP, zero, lane);
+            if (kh == 0) du = tile_mm<kC>(&sPs[0][0], 1, kP16, &sDO[0][16 * ct], kPS, 1, du, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sdU[kh][4 * g4 + i][16 * ct + r16] = du[i];
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            accKh[e] = tile_mm_kc<kCW>(&sU[0][0], kPS, &sG[16 * (2 * w + e)][0], kPS, zero, lane);
+        if (w == 3) {
+            const f32x4 dp = tile_mm_kc<kCW>(&sDO[0][0], kPS, &sU[0][0], kPS, zero, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * g4 + i;
+                sdP[r][r16] = r16 < r ? a.scale * dp[i] : 0.f;
+                if (r16 == r) sDPd[r] = a.scale * dp[i];
+            }
+        }
+        lds_barrier();
+
+        // (B2) dZ = M^T dU (waves 0, 1; it is dv); dM = dU Z^T and the solve's
+        // adjoint (wave 3)
+        if (w < 2) {
+            const int ct = w;
+            f32x4 dz = zero;
+#pragma unroll
+            for (int k0 = 0; k0 < kC; k0 += 4) {
+                const int k = k0 + g4;
+                dz = mfma4(sM[k][r16], sdU[0][k][16 * ct + r16] + sdU[1][k][16 * ct + r16], dz);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * g4 + i;
+                sdZ[t][16 * ct + r16] = dz[i];
+                st4(dvb, 4 * (static_cast<uint32_t>(t) * HD + 16 * ct + r16), dz[i]);
+            }
+        } else if (w == 3) {
+            // dM = dU Z^T, then back through the solve: T1 = dN N^T with
+            // dN = dM diag(beta), dA = -N^T T1, dGr and this slice's dbeta
+            f32x4 dm = zero;
+#pragma unroll
+            for (int k0 = 0; k0 < kCW; k0 += 4) {
+                const int k = k0 + g4;
+                dm = mfma4(sdU[0][r16][k] + sdU[1][r16][k], sZ[r16][k], dm);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sdM[4 * g4 + i][r16] = dm[i];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            f32x4 t1 = zero;
+#pragma unroll
+            for (int k0 = 0; k0 < kC; k0 += 4) {
+                const int k = k0 + g4;
+                t1 = mfma4(sdM[r16][k] * sBeta[k], sN[r16][k], t1);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sT1[4 * g4 + i][r16] = t1[i];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // dA = -N^T T1 (strictly lower part)
+            f32x4 na = zero;
+#pragma unroll
+            for (int k0 = 0; k0 < kC; k0 += 4) {
+                const int k = k0 + g4;
+                na = mfma4(sN[k][r16], sT1[k][r16], na);
+            }
+            float dbr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * g4 + i;
+                const float da = r16 < r ? -na[i] : 0.f;
+                sdGr[r][r16] = sBeta[r] * da;
+                dbr[i] = row_sum16(da * sGr[r][r16]);  // sum over s < r of dA_rs (Kb Kh^T)_rs
+            }
+            if (r16 == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sT1[4 * g4 + i][kC] = dbr[i];  // (column 16: padding)
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lane < kC) {
+                // dbeta_s = sum_r dM_rs N_rs + the A term of row s
+                float x = sT1[lane][kC];
+#pragma unroll
+                for (int r = 0; r < kC; ++r) x += sdM[r][lane] * sN[r][lane];
+                sDB[lane] = x;
+            }
+        }
+        lds_barrier();
+
+        // (B3) dS0 = G - Kb^T dZ + scale Qb^T dO (this wave's tiles: the next
+        // dS); dKb starts as -dZ S0^T
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int rb = 2 * w + (q >> 1), ct = q & 1;
+            const f32x4 t1 = tile_mm<kC>(&sKb[0][16 * rb], 1, kP, &sdZ[0][16 * ct], kPS, 1, zero, lane);
+            const f32x4 t2 = tile_mm<kC>(&sQb[0][16 * rb], 1, kP, &sDO[0][16 * ct], kPS, 1, zero, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dS[q][i] = (dS[q][i] - t1[i]) + a.scale * t2[i];
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            accKb[e] = tile_mm_kc<kCW>(&sdZ[0][0], kPS, &sS0[16 * (2 * w + e)][0], kPS, zero, lane);
+        lds_barrier();
+
+        // (B4) finish dQb, dKb, dKh on this wave's channel blocks; dq, dk and
+        // dgamma of its 16 tokens x 32 channels
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int cb = 2 * w + e;
+            f32x4 dqb = a.scale * accQ[e];
+            dqb = tile_mm<kC>(&sdP[0][0], kP16, 1, &sKh[0][16 * cb], kP, 1, dqb, lane);
+            f32x4 dkb = -accKb[e];
+            dkb = tile_mm<kC>(&sdGr[0][0], kP16, 1, &sKh[0][16 * cb], kP, 1, dkb, lane);
+            // the pairs' part of dKh on its own (the U G^T part is W, summed apart)
+            f32x4 dkh = tile_mm<kC>(&sdGr[0][0], 1, kP16, &sKb[0][16 * cb], kP, 1, zero, lane);
+            dkh = tile_mm<kC>(&sdP[0][0], 1, kP16, &sQb[0][16 * cb], kP, 1, dkh, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * g4 + i, c = 16 * cb + r16;
+                const float eg = sEg[t][c], egi = sEgi[t][c], kh = sKh[t][c], qb = sQb[t][c], kb = sKb[t][c];
+                sDgam[t][c] = (dqb[i] * qb + dkb[i] * kb) - dkh[i] * kh;
+                sW[t][c] = accKh[e][i] * kh;
+                const uint32_t o = 4 * (static_cast<uint32_t>(t) * HD + c);
+                const float dpd = sDPd[t];
+                st4(pq, o, dqb[i] * eg + dpd * (kb * egi));  // + dP_tt k_t
+                st4(pk, o, (dkb[i] * eg + (accKh[e][i] + dkh[i]) * egi) + dpd * (qb * egi));  // + dP_tt q_t
+            }
+        }
+        lds_barrier();
+
+        // dg: the suffix sums of dgamma over the chunk, the gamma_C term and the
+        // prefix sums of W; thread (c = tid % 128, h = tid / 128) writes tokens
+        // 8 h .. 8 h + 7 of channel c.  And this slice's share of dbeta.
+        {
+            const int c = tid & (D - 1), hh = tid >> 7;
+            float x = sDgC[c], y = 0.f;  // x: suffix of dgamma past these tokens; y: prefix of W before them
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                if (hh == 0) x += sDgam[8 + t][c];
+                else y += sW[t][c];
+            }
+            float pre[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                pre[t] = y;
+                y += sW[8 * hh + t][c];
+            }
+#pragma unroll
+            for (int t = 7; t >= 0; --t) {
+                const int tok = 8 * hh + t;
+                x += sDgam[tok][c];
+                st4(pg, 4 * (static_cast<uint32_t>(tok) * HD + c), x + pre[t]);
+            }
+            if (tid < kC) st4(pb, 4 * (static_cast<uint32_t>(tid) * static_cast<uint32_t>(H)), sDB[tid]);
+        }
+    }
+
+    if (a.dh0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int rb = 2 * w + (q >> 1), ct = q & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a.dh0[sb + (16 * rb + 4 * g4 + i) * D + col0 + 16 * ct + r16] = dS[q][i];
+        }
+    }
+}
+
 // A slice's partials are three planes of n_tok * D values (dq, dk, dg) and
 // then n_tok values (dbeta).
 __global__ void bwd_sum_kernel(const float *part, int64_t stride, int64_t plane, int ns, float *dq, float *dk,
@@ -540,8 +1163,14 @@ __global__ void bwd_sum_kernel(const float *part, int64_t stride, int64_t plane,
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
     const int64_t BH = a.B * a.H;
     if (a.D == 128) {
+        // bf16 inputs: the chunk form on the matrix cores.  fp32 inputs: the
+        // token-serial adjoint, whose dg is formed per token; in the chunk
+        // form dg sums pieces that partly cancel, which costs it about 1e-4
+        // of accuracy (relative to its rms) under strong decay or beta = 1.
+        // (the chunk kernel's 32-bit byte offsets need 16 H D 4 < 2^31)
         const dim3 grid(static_cast<unsigned>(BH * 4));
-        if (a.bf16) hipLaunchKernelGGL((bwd_col_kernel<true>), grid, dim3(512), 0, s, a);
+        if (a.bf16 && a.H < 65536) hipLaunchKernelGGL(bwd_chunk_kernel, grid, dim3(256), 0, s, a);
+        else if (a.bf16) hipLaunchKernelGGL((bwd_col_kernel<true>), grid, dim3(512), 0, s, a);
         else hipLaunchKernelGGL((bwd_col_kernel<false>), grid, dim3(512), 0, s, a);
     } else if (a.D == 16) {
         const dim3 grid(static_cast<unsigned>(BH));
