@@ -247,7 +247,7 @@ def time_backward(kda, torch, stream, steps, calibrate=False):
     return {"workload": cfg.name, "ms": avg, "min_ms": mn, "tokens_per_s": cfg.B * cfg.T / (avg * 1e-3),
             "alg_bytes_per_launch": nbytes, "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": gbps / HBM_PEAK_GBPS,
-            "note": "forward checkpoint pass + token-serial fp32 adjoint + slice sums; vector-ALU bound"}
+            "note": "forward checkpoint pass + chunk-form adjoint (fp32 MFMA) + slice sums; latency bound"}
 
 
 def copy_bandwidth(torch, stream, nbytes=1 << 30, steps=10):

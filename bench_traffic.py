@@ -208,7 +208,7 @@ def segmented(dt, out, n_seg):
 
 
 BWD_KERNELS = (("prefill_mfma_kernel<true, 0, 0>", "forward with a state checkpoint every 16 tokens"),
-               ("bwd_col_kernel<true>", "token-serial adjoint, 32-column slices"),
+               ("bwd_chunk_kernel", "chunk-form adjoint on fp32 matrix cores, 32-column slices"),
                ("bwd_sum_kernel", "sum of the slices' partial sums (dq, dk, dg, dbeta)"))
 
 

@@ -284,6 +284,11 @@ uint64_t kda_chunk_fwd_kcp_noalloc_max_bytes(void);
  * Results are deterministic (fixed summation order).  All other rules, the
  * layouts and the errors are those of kda_chunk_fwd; T == 0 writes dh0 = dhT
  * (or zeros).
+ *
+ * With bf16 inputs at Dk = 128 the gradient is computed in the 16-token chunk
+ * form on the fp32 matrix cores (the same values up to rounding; dg, formed
+ * from pieces that partly cancel, carries the largest error, about 1e-3 of
+ * its rms); fp32 inputs, and Dk = 16, take the token-by-token form above.
  */
 kda_status kda_chunk_bwd(const void *q, const void *k, const void *v,
                          const float *g, const float *beta, const float *h0,
