@@ -300,8 +300,9 @@ kda_status kda_chunk_bwd(const void *q, const void *k, const void *v,
 
 /*
  * kda_chunk_bwd_ws_bytes -- bytes of workspace kda_chunk_bwd needs:
- * floor(T / 16) states of [B, H, Dk, Dv] fp32 plus (3 Dk + 1) B T H fp32
- * partial sums per column slice (4 slices at Dk = 128, 1 at Dk = 16).
+ * floor(T / 16) states of [B, H, Dk, Dv] fp32 plus, per column slice (4
+ * slices at Dk = 128, 1 at Dk = 16), (3 Dk + 1) B T H fp32 partial sums
+ * rounded up to a multiple of 4.
  * 0 for unsupported or invalid sizes (Dk != Dv, Dk not 16 or 128, or 64-bit
  * overflow).
  */

@@ -402,7 +402,9 @@ uint64_t kda_chunk_bwd_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int
         return 0;
     if (!mul_ok(tok, B) || !mul_ok(tok, T) || !mul_ok(tok, H)) return 0;
     pt = tok;
-    if (!mul_ok(pt, 3 * Dk + 1) || !mul_ok(pt, ns)) return 0;
+    if (!mul_ok(pt, 3 * Dk + 1) || pt > UINT64_MAX - 3) return 0;
+    pt = (pt + 3) / 4 * 4;  // each slice's partials start 16-byte aligned
+    if (!mul_ok(pt, ns)) return 0;
     if (ck > UINT64_MAX / 8 || pt > UINT64_MAX / 8 || ck + pt > UINT64_MAX / 4) return 0;
     const uint64_t n = ck + pt;
     return n == 0 ? 16 : n * 4;
@@ -466,7 +468,7 @@ kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const floa
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
     a.part = ckpt + static_cast<uint64_t>(n_ck) * n_state;
     a.part_plane = static_cast<int64_t>(n_tok * Dk);
-    a.part_stride = static_cast<int64_t>(n_tok * (3 * Dk + 1));
+    a.part_stride = static_cast<int64_t>((n_tok * (3 * Dk + 1) + 3) / 4 * 4);  // as kda_chunk_bwd_ws_bytes
     a.B = B; a.T = T; a.H = H; a.D = static_cast<int>(Dk);
     a.bf16 = in_dtype == KDA_BF16;
     a.scale = fa.scale;

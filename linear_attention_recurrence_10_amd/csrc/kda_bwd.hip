@@ -26,6 +26,8 @@
 // row; a sum over the rows of a column is a register sum, shuffles among the
 // 8 lanes of the column within the wave, and one exchange of the waves'
 // partial sums through LDS.
+#include <type_traits>
+
 #include "kda_internal.h"
 
 namespace kda {
@@ -1143,18 +1145,30 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     }
 }
 
-// A slice's partials are three planes of n_tok * D values (dq, dk, dg) and
-// then n_tok values (dbeta).
-__global__ void bwd_sum_kernel(const float *part, int64_t stride, int64_t plane, int ns, float *dq, float *dk,
-                               float *dg, float *dbeta, int64_t n_tok) {
-    for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < 3 * plane + n_tok;
-         e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        float s = 0.f;
-        for (int sl = 0; sl < ns; ++sl) s += part[sl * stride + e];
-        if (e < plane) dq[e] = s;
-        else if (e < 2 * plane) dk[e - plane] = s;
-        else if (e < 3 * plane) dg[e - 2 * plane] = s;
-        else dbeta[e - 3 * plane] = s;
+// A slice's partials are three planes of n_tok * D values (dq, dk, dg), then
+// n_tok values (dbeta); slices start `stride` floats apart (a multiple of 4,
+// so every plane of every slice starts 16-byte aligned).  The planes are
+// summed four values at a time when dq, dk and dg are 16-byte aligned too
+// (a plane holds a multiple of 16 values, so a group never straddles two).
+template <bool VEC>
+__global__ __launch_bounds__(256) void bwd_sum_kernel(const float *part, int64_t stride, int64_t plane, int ns,
+                                                      float *dq, float *dk, float *dg, float *dbeta, int64_t n_tok) {
+    constexpr int W = VEC ? 4 : 1;
+    using V = std::conditional_t<VEC, f32x4, float>;
+    const int64_t n_vec = 3 * plane / W, step = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n_vec + n_tok; e += step) {
+        if (e < n_vec) {
+            V s = *reinterpret_cast<const V *>(part + W * e);
+            for (int sl = 1; sl < ns; ++sl) s += *reinterpret_cast<const V *>(part + sl * stride + W * e);
+            const int64_t x = W * e;
+            float *dst = x < plane ? dq + x : x < 2 * plane ? dk + (x - plane) : dg + (x - 2 * plane);
+            __builtin_nontemporal_store(s, reinterpret_cast<V *>(dst));
+        } else {
+            const int64_t t = e - n_vec;
+            float s = part[3 * plane + t];
+            for (int sl = 1; sl < ns; ++sl) s += part[sl * stride + 3 * plane + t];
+            dbeta[t] = s;
+        }
     }
 }
 
@@ -1182,11 +1196,17 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n_tok = a.B * a.T * a.H;
-    const int64_t total = 3 * a.part_plane + n_tok;
+    const bool vec = ((reinterpret_cast<uintptr_t>(a.dq) | reinterpret_cast<uintptr_t>(a.dk) |
+                       reinterpret_cast<uintptr_t>(a.dg)) & 15) == 0;
+    const int64_t total = 3 * a.part_plane / (vec ? 4 : 1) + n_tok;
     const int64_t blocks = (total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192;
-    if (blocks > 0)
-        hipLaunchKernelGGL(bwd_sum_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a.part,
-                           a.part_stride, a.part_plane, a.D == 128 ? 4 : 1, a.dq, a.dk, a.dg, a.dbeta, n_tok);
+    const int ns = a.D == 128 ? 4 : 1;
+    if (blocks > 0 && vec)
+        hipLaunchKernelGGL(bwd_sum_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a.part,
+                           a.part_stride, a.part_plane, ns, a.dq, a.dk, a.dg, a.dbeta, n_tok);
+    else if (blocks > 0)
+        hipLaunchKernelGGL(bwd_sum_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a.part,
+                           a.part_stride, a.part_plane, ns, a.dq, a.dk, a.dg, a.dbeta, n_tok);
     return hipGetLastError();
 }
 

@@ -273,9 +273,11 @@ def bwd(lib, B=1, T=16, H=1, Dk=128, Dv=128, ws_bytes=1 << 30, ptrs=None):
 
 
 def test_bwd_workspace_size(lib):
-    # floor(T / 16) states plus (3 D + 1) B T H partials per slice (4 slices at D = 128)
+    # floor(T / 16) states plus (3 D + 1) B T H partials per slice (4 slices at D = 128),
+    # each slice rounded up to a multiple of 4 floats
     assert lib.kda_chunk_bwd_ws_bytes(1, 64, 2, 128, 128) == 4 * (4 * 2 * 128 * 128 + 4 * 64 * 2 * (3 * 128 + 1))
-    assert lib.kda_chunk_bwd_ws_bytes(2, 17, 3, 16, 16) == 4 * (1 * 6 * 16 * 16 + 1 * 2 * 17 * 3 * (3 * 16 + 1))
+    assert lib.kda_chunk_bwd_ws_bytes(2, 17, 3, 16, 16) == 4 * (1 * 6 * 16 * 16 + 1 * 2 * 17 * 3 * (3 * 16 + 1) + 2)
+    assert lib.kda_chunk_bwd_ws_bytes(1, 17, 1, 128, 128) == 4 * (128 * 128 + 4 * (17 * 385 + 3))
     assert lib.kda_chunk_bwd_ws_bytes(1, 16, 1, 128, 64) == 0
     assert lib.kda_chunk_bwd_ws_bytes(1, 16, 1, 64, 64) == 0
     assert lib.kda_chunk_bwd_ws_bytes(0, 16, 1, 128, 128) == 0
