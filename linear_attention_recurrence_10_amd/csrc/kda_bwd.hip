@@ -623,12 +623,13 @@ __device__ __forceinline__ void bwd_pivots(float &x, const float (&nar)[16]) {
     }
 }
 
-// The inputs of one chunk for thread tid, in registers: token t = tid / 16,
-// channels 8 p .. 8 p + 7 (p = tid % 16) of q, k (bf16) and g; v of the slice
-// (token (tid % 64) / 4, columns 8 (tid % 4) ..); dO of the slice (with
-// d = (tid - 64) % 128: token d / 8, columns 4 (d % 8) ..); the state before
-// the chunk, rows tid / 8 + 32 m, columns 4 (tid % 8) ..; beta of token
-// tid % 16.
+// The inputs of one chunk for thread tid (wave w = tid / 64, lane l), in
+// registers: token l % 16, channels 32 w + 8 (l / 16) .. + 7 of q, k (bf16)
+// and g, so that each 16-lane row holds all 16 tokens of its 8 channels; v of
+// the slice (token (tid % 64) / 4, columns 8 (tid % 4) ..); dO of the slice
+// (with d = (tid - 64) % 128: token d / 8, columns 4 (d % 8) ..); the state
+// before the chunk, rows tid / 8 + 32 m, columns 4 (tid % 8) ..; beta of
+// token tid % 16.
 struct ChunkIn {
     uint4 q, k, v;
     float4 g0, g1, dO, s00, s01, s02, s03;
@@ -666,8 +667,7 @@ __device__ __forceinline__ ChunkIn load_chunk_inputs(const BwdArgs &a, int64_t t
                                                      const float *s0, int64_t sb, int tid) {
     constexpr int D = 128;
     const uint32_t H = static_cast<uint32_t>(a.H), HD = H * D, last = static_cast<uint32_t>(nt - 1) * HD;
-    const int t = tid >> 4, p = tid & 15;
-    const uint32_t off = static_cast<uint32_t>(t) * HD + 8 * p;  // elements
+    const uint32_t off = static_cast<uint32_t>(tid & 15) * HD + 32 * (tid >> 6) + 8 * ((tid >> 4) & 3);  // elements
     const Rsrc rq = buf(static_cast<const uint16_t *>(a.q) + tok0 * D, 2 * (last + D));
     const Rsrc rk = buf(static_cast<const uint16_t *>(a.k) + tok0 * D, 2 * (last + D));
     const Rsrc rg = buf(a.g + tok0 * D, 4 * (last + D));
@@ -710,36 +710,53 @@ __device__ __forceinline__ void put_row4(float (*sS0)[PS], float (*sS0T)[P], int
     sS0T[j + 3][c] = x.w;
 }
 
+// The chunk's inputs to LDS.  q, k and g become the operands at once: the
+// cumulative log-decay gamma of each channel over the tokens (a prefix sum
+// across the 16 lanes of a row), e^gamma and e^-gamma, Qb = q e^gamma,
+// Kb = k e^gamma and Kh = k e^-gamma.  Tokens past the end were loaded as
+// zeros, so they have zero operands and keep the last token's gamma.
 template <int P, int PS>
-__device__ __forceinline__ void store_chunk_inputs(const ChunkIn &in, int nt, int tid, float (*sQ)[P], float (*sK)[P],
-                                                   float (*sG)[P], float (*sV)[PS], float (*sDO)[PS], float (*sS0)[PS],
-                                                   float (*sS0T)[P], float *sBeta) {
-    const int t = tid >> 4, c = 8 * (tid & 15);
-    const bool live = t < nt;
-    sQ[t][c + 0] = live ? bf_lo(in.q.x) : 0.f;
-    sQ[t][c + 1] = live ? bf_hi(in.q.x) : 0.f;
-    sQ[t][c + 2] = live ? bf_lo(in.q.y) : 0.f;
-    sQ[t][c + 3] = live ? bf_hi(in.q.y) : 0.f;
-    sQ[t][c + 4] = live ? bf_lo(in.q.z) : 0.f;
-    sQ[t][c + 5] = live ? bf_hi(in.q.z) : 0.f;
-    sQ[t][c + 6] = live ? bf_lo(in.q.w) : 0.f;
-    sQ[t][c + 7] = live ? bf_hi(in.q.w) : 0.f;
-    sK[t][c + 0] = live ? bf_lo(in.k.x) : 0.f;
-    sK[t][c + 1] = live ? bf_hi(in.k.x) : 0.f;
-    sK[t][c + 2] = live ? bf_lo(in.k.y) : 0.f;
-    sK[t][c + 3] = live ? bf_hi(in.k.y) : 0.f;
-    sK[t][c + 4] = live ? bf_lo(in.k.z) : 0.f;
-    sK[t][c + 5] = live ? bf_hi(in.k.z) : 0.f;
-    sK[t][c + 6] = live ? bf_lo(in.k.w) : 0.f;
-    sK[t][c + 7] = live ? bf_hi(in.k.w) : 0.f;
-    sG[t][c + 0] = live ? in.g0.x : 0.f;
-    sG[t][c + 1] = live ? in.g0.y : 0.f;
-    sG[t][c + 2] = live ? in.g0.z : 0.f;
-    sG[t][c + 3] = live ? in.g0.w : 0.f;
-    sG[t][c + 4] = live ? in.g1.x : 0.f;
-    sG[t][c + 5] = live ? in.g1.y : 0.f;
-    sG[t][c + 6] = live ? in.g1.z : 0.f;
-    sG[t][c + 7] = live ? in.g1.w : 0.f;
+__device__ __forceinline__ void store_chunk_inputs(const ChunkIn &in, int nt, int tid, float (*sQb)[P],
+                                                   float (*sKb)[P], float (*sKh)[P], float (*sEg)[P],
+                                                   float (*sEgi)[P], float (*sV)[PS], float (*sDO)[PS],
+                                                   float (*sS0)[PS], float (*sS0T)[P], float *sBeta) {
+    {
+        const int t = tid & 15, c0 = 32 * (tid >> 6) + 8 * ((tid >> 4) & 3);
+        float gam[8] = {in.g0.x, in.g0.y, in.g0.z, in.g0.w, in.g1.x, in.g1.y, in.g1.z, in.g1.w};
+        // prefix sums over the 16 tokens of the row (lanes before the row's
+        // start read 0), shift-major so each DPP source was written earlier
+#pragma unroll
+        for (int j = 0; j < 8; ++j) gam[j] += dpp_mv<0x111>(gam[j]);  // row_shr:1
+#pragma unroll
+        for (int j = 0; j < 8; ++j) gam[j] += dpp_mv<0x112>(gam[j]);  // row_shr:2
+#pragma unroll
+        for (int j = 0; j < 8; ++j) gam[j] += dpp_mv<0x114>(gam[j]);  // row_shr:4
+#pragma unroll
+        for (int j = 0; j < 8; ++j) gam[j] += dpp_mv<0x118>(gam[j]);  // row_shr:8
+        const uint32_t qw[4] = {in.q.x, in.q.y, in.q.z, in.q.w}, kw[4] = {in.k.x, in.k.y, in.k.z, in.k.w};
+        float qb[8], kb[8], kh[8], eg[8], egi[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float e = __expf(gam[j]), ei = __expf(-gam[j]);
+            const float qv = (j & 1) ? bf_hi(qw[j >> 1]) : bf_lo(qw[j >> 1]);
+            const float kv = (j & 1) ? bf_hi(kw[j >> 1]) : bf_lo(kw[j >> 1]);
+            qb[j] = qv * e;
+            kb[j] = kv * e;
+            kh[j] = kv * ei;
+            eg[j] = e;
+            egi[j] = ei;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c = c0 + 4 * h;
+            *reinterpret_cast<f32x4 *>(&sQb[t][c]) = f32x4{qb[4 * h], qb[4 * h + 1], qb[4 * h + 2], qb[4 * h + 3]};
+            *reinterpret_cast<f32x4 *>(&sKb[t][c]) = f32x4{kb[4 * h], kb[4 * h + 1], kb[4 * h + 2], kb[4 * h + 3]};
+            *reinterpret_cast<f32x4 *>(&sKh[t][c]) = f32x4{kh[4 * h], kh[4 * h + 1], kh[4 * h + 2], kh[4 * h + 3]};
+            *reinterpret_cast<f32x4 *>(&sEg[t][c]) = f32x4{eg[4 * h], eg[4 * h + 1], eg[4 * h + 2], eg[4 * h + 3]};
+            *reinterpret_cast<f32x4 *>(&sEgi[t][c]) =
+                f32x4{egi[4 * h], egi[4 * h + 1], egi[4 * h + 2], egi[4 * h + 3]};
+        }
+    }
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (wv == 0) {
         const int vt = tid >> 2, vc = 8 * (tid & 3);
@@ -790,7 +807,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     __shared__ float sS0T[kCW][kP], sGT[kCW][kP];  // transposed copies: column j, channel c
     __shared__ float sV[kC][kPS], sDO[kC][kPS], sZ[kC][kPS], sU[kC][kPS], sdU[2][kC][kPS], sdZ[kC][kPS];
     __shared__ float sA[kC][kP16], sGr[kC][kP16], sPs[kC][kP16], sN[kC][kP16], sM[kC][kP16];
-    __shared__ float sdM[kC][kP16], sdP[kC][kP16], sdGr[kC][kP16], sT1[kC][kP16];
+    __shared__ float sdP[kC][kP16], sdGr[kC][kP16];
     __shared__ float sBeta[kC], sDgC[D], sDB[kC], sDPd[kC];
 
     const int64_t bh = blockIdx.x / kNS;
@@ -816,6 +833,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
         for (int i = 0; i < 4; ++i)
             dS[q][i] = a.dhT ? a.dhT[sb + (16 * rb + 4 * g4 + i) * D + col0 + 16 * ct + r16] : 0.f;
     }
+    // (dS has landed before the loop: without this wait the loop would wait for
+    // every outstanding store, once per chunk, where it first scales dS)
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
     const int64_t nch = (T + kC - 1) / kC;
     ChunkIn in{};
@@ -844,48 +864,10 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
         lds_barrier();  // the previous chunk is done with LDS
 
         // (L) the chunk's inputs, loaded during the previous chunk (or before
-        //     the loop), to LDS: q, k and g land in sQb, sKb and sKh, which the
-        //     pass after the barrier turns into Qb, Kb, Kh
-        store_chunk_inputs(in, nt, tid, sQb, sKb, sKh, sV, sDO, sS0, sS0T, sBeta);
+        //     the loop), to LDS: the decay factors and the scaled operands
+        //     Qb, Kb, Kh are formed on the way (e^gamma_C is row 15 of sEg)
+        store_chunk_inputs(in, nt, tid, sQb, sKb, sKh, sEg, sEgi, sV, sDO, sS0, sS0T, sBeta);
         lds_barrier();
-        // the next chunk's loads are in flight while this one is worked on
-        // (in the last step, chunk 0 again: the loads are the same every step)
-        {
-            const int64_t np = n > 0 ? n - 1 : 0;
-            in = load_chunk_inputs(a, (b * T + np * kC) * H + h, n > 0 ? kC : nt, col0,
-                                   np == 0 ? a.h0 : a.ckpt + (np - 1) * BHD, sb, tid);
-        }
-        // the cumulative log-decay, in place of g (a thread per channel) ...
-        if (tid < D) {
-            float gv[kC];
-#pragma unroll
-            for (int t = 0; t < kC; ++t) gv[t] = sKh[t][tid];
-            float gam = 0.f;
-#pragma unroll
-            for (int t = 0; t < kC; ++t) {
-                gam += gv[t];
-                sKh[t][tid] = gam;
-            }
-        }
-        lds_barrier();
-        // ... then the decay factors and the scaled operands, thread (t = tid /
-        // 16, channels 8 (tid % 16) ..); e^gamma_C is row 15 of sEg
-        {
-            const int t = tid >> 4, c0 = 8 * (tid & 15);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int c = c0 + j;
-                const float gam = sKh[t][c], qv = sQb[t][c], kv = sKb[t][c];
-                const float e = __expf(gam), ei = __expf(-gam);
-                sQb[t][c] = qv * e;
-                sKb[t][c] = kv * e;
-                sKh[t][c] = kv * ei;
-                sEg[t][c] = e;
-                sEgi[t][c] = ei;
-            }
-        }
-        lds_barrier();
-
         // (F1) Kb Kh^T and A (wave 0), scale P (wave 1), Z = V - Kb S0 (waves 2, 3)
         if (w == 0) {
             const f32x4 gr = tile_mm_kc<D>(&sKb[0][0], kP, &sKh[0][0], kP, zero, lane);
@@ -1011,62 +993,48 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
                 st4(dvb, 4 * (static_cast<uint32_t>(t) * HD + 16 * ct + r16), dz[i]);
             }
         } else if (w == 3) {
-            // dM = dU Z^T, then back through the solve: T1 = dN N^T with
-            // dN = dM diag(beta), dA = -N^T T1, dGr and this slice's dbeta
-            f32x4 dm = zero;
+            // dM^T = Z dU^T, then back through the solve: T1 = dN N^T with
+            // dN = dM diag(beta), dA = -N^T T1, dGr and this slice's dbeta.
+            // Each product's result feeds the next one from registers: lane
+            // (r16, g4) holds rows 4 g4 + i of column r16 of a result, which
+            // are that lane's operand values when the next product takes
+            // k = 4 g4 + m at step m (the order of a sum over k is free).
+            f32x4 dmt = zero;  // lane (r16, g4): dM(r16, 4 g4 + i)
 #pragma unroll
             for (int k0 = 0; k0 < kCW; k0 += 4) {
                 const int k = k0 + g4;
-                dm = mfma4(sdU[0][r16][k] + sdU[1][r16][k], sZ[r16][k], dm);
+                dmt = mfma4(sZ[r16][k], sdU[0][r16][k] + sdU[1][r16][k], dmt);
             }
+            f32x4 t1 = zero;  // T1(4 g4 + i, r16) = sum_s dM(4 g4 + i, s) beta_s N(r16, s)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sdM[4 * g4 + i][r16] = dm[i];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            f32x4 t1 = zero;
-#pragma unroll
-            for (int k0 = 0; k0 < kC; k0 += 4) {
-                const int k = k0 + g4;
-                t1 = mfma4(sdM[r16][k] * sBeta[k], sN[r16][k], t1);
+            for (int m = 0; m < 4; ++m) {
+                const int sk = 4 * g4 + m;
+                t1 = mfma4(dmt[m] * sBeta[sk], sN[r16][sk], t1);
             }
+            f32x4 na = zero;  // (N^T T1)(4 g4 + i, r16)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sT1[4 * g4 + i][r16] = t1[i];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // dA = -N^T T1 (strictly lower part)
-            f32x4 na = zero;
-#pragma unroll
-            for (int k0 = 0; k0 < kC; k0 += 4) {
-                const int k = k0 + g4;
-                na = mfma4(sN[k][r16], sT1[k][r16], na);
-            }
-            float dbr[4];
+            for (int m = 0; m < 4; ++m) na = mfma4(sN[4 * g4 + m][r16], t1[m], na);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * g4 + i;
                 const float da = r16 < r ? -na[i] : 0.f;
                 sdGr[r][r16] = sBeta[r] * da;
-                dbr[i] = row_sum16(da * sGr[r][r16]);  // sum over s < r of dA_rs (Kb Kh^T)_rs
-            }
-            if (r16 == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sT1[4 * g4 + i][kC] = dbr[i];  // (column 16: padding)
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (lane < kC) {
-                // dbeta_s = sum_r dM_rs N_rs + the A term of row s
-                float x = sT1[lane][kC];
-#pragma unroll
-                for (int r = 0; r < kC; ++r) x += sdM[r][lane] * sN[r][lane];
-                sDB[lane] = x;
+                // dbeta_r = sum over rows u of dM_ur N_ur (column r of dM .* N) plus
+                // sum over s < r of dA_rs (Kb Kh^T)_rs (row r of dA .* Gr)
+                const float db = row_sum16(dmt[i] * sN[r16][r]) + row_sum16(da * sGr[r][r16]);
+                if (r16 == 0) sDB[r] = db;
             }
         }
         lds_barrier();
 
+        // the next chunk's loads, issued among the products of B3 (straight-line
+        // code in every wave), are in flight through B4 and the dg pass (in the
+        // last step, chunk 0 again: the loads are the same every step)
+        {
+            const int64_t np = n > 0 ? n - 1 : 0;
+            in = load_chunk_inputs(a, (b * T + np * kC) * H + h, n > 0 ? kC : nt, col0,
+                                   np == 0 ? a.h0 : a.ckpt + (np - 1) * BHD, sb, tid);
+        }
         // (B3) dS0 = G - Kb^T dZ + scale Qb^T dO (this wave's tiles: the next
         // dS); dKb starts as -dZ S0^T
 #pragma unroll
