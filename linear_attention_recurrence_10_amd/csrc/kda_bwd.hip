@@ -660,6 +660,9 @@ __device__ __forceinline__ float4 ld16f(Rsrc r, uint32_t off) {
 __device__ __forceinline__ void st4(Rsrc r, uint32_t off, float x) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
 }
+__device__ __forceinline__ void st16(Rsrc r, uint32_t off, f32x4 x) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
+}
 
 // tok0: row of token t0 of this (b, h) in [B, T, H] rows; nt: valid tokens
 // of the chunk; s0: the state before the chunk (null: zero).
@@ -918,7 +921,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
         f32x4 accQ[2], accKb[2], accKh[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-            accQ[e] = tile_mm_kc<kCW>(&sDO[0][0], kPS, &sS0[16 * (2 * w + e)][0], kPS, zero, lane);
+            accQ[e] = tile_mm_kc<kCW>(&sS0[16 * (2 * w + e)][0], kPS, &sDO[0][0], kPS, zero, lane);
 
         // (F4) G = D_C dS (kept in dS and written for the products) and the
         // gamma_C term of D_C S0: rowsum(S0 .* G)
@@ -964,7 +967,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-            accKh[e] = tile_mm_kc<kCW>(&sU[0][0], kPS, &sG[16 * (2 * w + e)][0], kPS, zero, lane);
+            accKh[e] = tile_mm_kc<kCW>(&sG[16 * (2 * w + e)][0], kPS, &sU[0][0], kPS, zero, lane);
         if (w == 3) {
             const f32x4 dp = tile_mm_kc<kCW>(&sDO[0][0], kPS, &sU[0][0], kPS, zero, lane);
 #pragma unroll
@@ -1047,57 +1050,79 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-            accKb[e] = tile_mm_kc<kCW>(&sdZ[0][0], kPS, &sS0[16 * (2 * w + e)][0], kPS, zero, lane);
+            accKb[e] = tile_mm_kc<kCW>(&sS0[16 * (2 * w + e)][0], kPS, &sdZ[0][0], kPS, zero, lane);
         lds_barrier();
 
         // (B4) finish dQb, dKb, dKh on this wave's channel blocks; dq, dk and
-        // dgamma of its 16 tokens x 32 channels
+        // dgamma of its 16 tokens x 32 channels.  The tiles are transposed
+        // (channel rows, token columns; the accumulators above likewise), so
+        // lane (r16, g4) holds channels 4 g4 .. 4 g4 + 3 of token r16: its LDS
+        // reads and writes and its partial stores are 16 bytes each.
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int cb = 2 * w + e;
             f32x4 dqb = a.scale * accQ[e];
-            dqb = tile_mm<kC>(&sdP[0][0], kP16, 1, &sKh[0][16 * cb], kP, 1, dqb, lane);
+            dqb = tile_mm<kC>(&sKh[0][16 * cb], 1, kP, &sdP[0][0], 1, kP16, dqb, lane);
             f32x4 dkb = -accKb[e];
-            dkb = tile_mm<kC>(&sdGr[0][0], kP16, 1, &sKh[0][16 * cb], kP, 1, dkb, lane);
+            dkb = tile_mm<kC>(&sKh[0][16 * cb], 1, kP, &sdGr[0][0], 1, kP16, dkb, lane);
             // the pairs' part of dKh on its own (the U G^T part is W, summed apart)
-            f32x4 dkh = tile_mm<kC>(&sdGr[0][0], 1, kP16, &sKb[0][16 * cb], kP, 1, zero, lane);
-            dkh = tile_mm<kC>(&sdP[0][0], 1, kP16, &sQb[0][16 * cb], kP, 1, dkh, lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 4 * g4 + i, c = 16 * cb + r16;
-                const float eg = sEg[t][c], egi = sEgi[t][c], kh = sKh[t][c], qb = sQb[t][c], kb = sKb[t][c];
-                sDgam[t][c] = (dqb[i] * qb + dkb[i] * kb) - dkh[i] * kh;
-                sW[t][c] = accKh[e][i] * kh;
-                const uint32_t o = 4 * (static_cast<uint32_t>(t) * HD + c);
-                const float dpd = sDPd[t];
-                st4(pq, o, dqb[i] * eg + dpd * (kb * egi));  // + dP_tt k_t
-                st4(pk, o, (dkb[i] * eg + (accKh[e][i] + dkh[i]) * egi) + dpd * (qb * egi));  // + dP_tt q_t
-            }
+            f32x4 dkh = tile_mm<kC>(&sKb[0][16 * cb], 1, kP, &sdGr[0][0], kP16, 1, zero, lane);
+            dkh = tile_mm<kC>(&sQb[0][16 * cb], 1, kP, &sdP[0][0], kP16, 1, dkh, lane);
+            const int t = r16, c = 16 * cb + 4 * g4;
+            const f32x4 eg = *reinterpret_cast<const f32x4 *>(&sEg[t][c]);
+            const f32x4 egi = *reinterpret_cast<const f32x4 *>(&sEgi[t][c]);
+            const f32x4 kh = *reinterpret_cast<const f32x4 *>(&sKh[t][c]);
+            const f32x4 qb = *reinterpret_cast<const f32x4 *>(&sQb[t][c]);
+            const f32x4 kb = *reinterpret_cast<const f32x4 *>(&sKb[t][c]);
+            const float dpd = sDPd[t];
+            *reinterpret_cast<f32x4 *>(&sDgam[t][c]) = (dqb * qb + dkb * kb) - dkh * kh;
+            *reinterpret_cast<f32x4 *>(&sW[t][c]) = accKh[e] * kh;
+            const uint32_t o = 4 * (static_cast<uint32_t>(t) * HD + c);
+            st16(pq, o, dqb * eg + dpd * (kb * egi));                            // + dP_tt k_t
+            st16(pk, o, (dkb * eg + (accKh[e] + dkh) * egi) + dpd * (qb * egi));  // + dP_tt q_t
         }
         lds_barrier();
 
         // dg: the suffix sums of dgamma over the chunk, the gamma_C term and the
-        // prefix sums of W; thread (c = tid % 128, h = tid / 128) writes tokens
-        // 8 h .. 8 h + 7 of channel c.  And this slice's share of dbeta.
+        // prefix sums of W (all before token t), as scans across the 16 lanes
+        // of a row: lane (t = tid % 16) of row j of wave w holds token t of
+        // channels 32 w + 8 j .. + 7 (lanes past the row's end read 0).  And
+        // this slice's share of dbeta.
         {
-            const int c = tid & (D - 1), hh = tid >> 7;
-            float x = sDgC[c], y = 0.f;  // x: suffix of dgamma past these tokens; y: prefix of W before them
+            const int t = tid & 15, c0 = 32 * w + 8 * ((tid >> 4) & 3);
+            float x[8], y[8];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                if (hh == 0) x += sDgam[8 + t][c];
-                else y += sW[t][c];
+            for (int h = 0; h < 2; ++h) {
+                const f32x4 d = *reinterpret_cast<const f32x4 *>(&sDgam[t][c0 + 4 * h]);
+                const f32x4 ww = *reinterpret_cast<const f32x4 *>(&sW[t][c0 + 4 * h]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[4 * h + i] = d[i];
+                    y[4 * h + i] = dpp_mv<0x111>(ww[i]);  // row_shr:1: W of token t - 1
+                }
             }
-            float pre[8];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                pre[t] = y;
-                y += sW[8 * hh + t][c];
-            }
+            for (int j = 0; j < 8; ++j) x[j] += dpp_mv<0x101>(x[j]);  // row_shl:1
 #pragma unroll
-            for (int t = 7; t >= 0; --t) {
-                const int tok = 8 * hh + t;
-                x += sDgam[tok][c];
-                st4(pg, 4 * (static_cast<uint32_t>(tok) * HD + c), x + pre[t]);
+            for (int j = 0; j < 8; ++j) y[j] += dpp_mv<0x111>(y[j]);  // row_shr:1
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] += dpp_mv<0x102>(x[j]);  // row_shl:2
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[j] += dpp_mv<0x112>(y[j]);  // row_shr:2
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] += dpp_mv<0x104>(x[j]);  // row_shl:4
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[j] += dpp_mv<0x114>(y[j]);  // row_shr:4
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] += dpp_mv<0x108>(x[j]);  // row_shl:8
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[j] += dpp_mv<0x118>(y[j]);  // row_shr:8
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f32x4 dg;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dg[i] = (x[4 * h + i] + sDgC[c0 + 4 * h + i]) + y[4 * h + i];
+                st16(pg, 4 * (static_cast<uint32_t>(t) * HD + c0 + 4 * h), dg);
             }
             if (tid < kC) st4(pb, 4 * (static_cast<uint32_t>(tid) * static_cast<uint32_t>(H)), sDB[tid]);
         }
