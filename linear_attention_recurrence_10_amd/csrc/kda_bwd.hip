@@ -864,7 +864,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
         const Rsrc pk = buf(part + a.part_plane + tok0 * D, 4 * (last + D));
         const Rsrc pg = buf(part + 2 * a.part_plane + tok0 * D, 4 * (last + D));
         const Rsrc pb = buf(part + 3 * a.part_plane + tok0, 4 * (static_cast<uint32_t>(nt - 1) * static_cast<uint32_t>(H) + 1));
-        lds_barrier();  // the previous chunk is done with LDS
+        // (no barrier here: the dg pass of the previous chunk reads only sDgam,
+        // sW, sDgC and sDB, which the store below leaves alone, and the barrier
+        // before that pass already ordered B4's reads of the operands)
 
         // (L) the chunk's inputs, loaded during the previous chunk (or before
         //     the loop), to LDS: the decay factors and the scaled operands
@@ -911,8 +913,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
         }
         lds_barrier();
 
-        // (F3) U = M Z (waves 0, 1); every wave starts its dQb tiles: dO S0^T
-        // (this wave's channel blocks cb = 2 w + e)
+        // (F3) U = M Z (waves 0, 1); every wave starts its dQb tiles, dO S0^T
+        // (transposed: this wave's channel blocks cb = 2 w + e as rows)
         if (w < 2) {
             const f32x4 uu = tile_mm<kC>(&sM[0][0], kP16, 1, &sZ[0][16 * w], kPS, 1, zero, lane);
 #pragma unroll
@@ -1051,7 +1053,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 2; ++e)
             accKb[e] = tile_mm_kc<kCW>(&sS0[16 * (2 * w + e)][0], kPS, &sdZ[0][0], kPS, zero, lane);
-        lds_barrier();
+        // (B3 writes no LDS: B4 follows without a barrier)
 
         // (B4) finish dQb, dKb, dKh on this wave's channel blocks; dq, dk and
         // dgamma of its 16 tokens x 32 channels.  The tiles are transposed
