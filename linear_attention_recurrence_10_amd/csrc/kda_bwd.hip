@@ -933,20 +933,19 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
             for (int e = 0; e < 2; ++e)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dgc[e][i] = 0.f;
+            // (rows 4 g4 .. 4 g4 + 3 of a tile are consecutive in sEg's last row,
+            // in sS0T and in sGT: one 16-byte access each)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int rb = 2 * w + (q >> 1), ct = q & 1;
-                f32x4 s0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s0[i] = sS0[16 * rb + 4 * g4 + i][16 * ct + r16];
+                const int rb = 2 * w + (q >> 1), ct = q & 1, row0 = 16 * rb + 4 * g4, col = 16 * ct + r16;
+                const f32x4 s0 = *reinterpret_cast<const f32x4 *>(&sS0T[col][row0]);
+                dS[q] *= *reinterpret_cast<const f32x4 *>(&sEg[kC - 1][row0]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * rb + 4 * g4 + i;
-                    dS[q][i] *= sEg[kC - 1][row];
                     dgc[q >> 1][i] += s0[i] * dS[q][i];
-                    sG[row][16 * ct + r16] = dS[q][i];
-                    sGT[16 * ct + r16][row] = dS[q][i];
+                    sG[row0 + i][col] = dS[q][i];
                 }
+                *reinterpret_cast<f32x4 *>(&sGT[col][row0]) = dS[q];
             }
 #pragma unroll
             for (int e = 0; e < 2; ++e)
