@@ -21,6 +21,8 @@ usage: python3 bench_traffic.py DIR_T DIR_F DIR_W OUT
            bench.py --segmented-only: OUT/kda_prefill_256k_h7_segmented_rocprof.md)
        python3 bench_traffic.py --util DIR_U OUT   (issue and pipe utilisation of the
            prefill from one counter run: OUT/kda_prefill_64k_util.md)
+       python3 bench_traffic.py --backward-util DIR_U OUT   (the same for the
+           backward's chunk kernel: OUT/kda_bwd_b4_h16_t4096_util.md)
        python3 bench_traffic.py --backward DIR_T DIR_F DIR_W OUT   (trace and traffic of
            bench.py --backward-only: OUT/kda_bwd_b4_h16_t4096_rocprof.md)
 """
@@ -310,7 +312,55 @@ def utilisation(du, out, cus=256, simds_per_cu=4, xcds=8):
     print("\n".join(lines))
 
 
+def backward_utilisation(du, out, cus=256, simds_per_cu=4, xcds=8):
+    """The same counters for the backward's chunk kernel (B=4 H=16 T=4096:
+    256 work-groups of four waves, one wave per SIMD, 256 chunks each):
+
+    rocprofv3 --pmc <UTIL_COUNTERS> --output-format csv -d DIR_U -o util -- \
+        python3 bench.py --backward-only --steps 2
+    """
+    import collections
+    rows = _csv(du, "counter_collection.csv")
+    per = collections.defaultdict(list)
+    for r in rows:
+        if "bwd_chunk_kernel" in r["Kernel_Name"]:
+            per[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    m = {k: statistics.mean(v) for k, v in per.items()}
+    active = m["GRBM_GUI_ACTIVE"] / xcds
+    chunks, wgs = 4096 // 16, 4 * 16 * 4
+    per_chunk_simd = lambda c: m[c] / (wgs * simds_per_cu * chunks)
+    cmd = ("rocprofv3 --pmc %s --output-format csv -d DIR_U -o util -- python3 bench.py --backward-only --steps 2"
+           % UTIL_COUNTERS)
+    mfma = per_chunk_simd("SQ_INSTS_MFMA")
+    lines = ["# rocprofv3: KDA backward chunk kernel (B=4 H=16 T=4096 d=128) issue and pipe utilisation", "",
+             "Commands (from the repository root):", "", "    " + cmd,
+             "    python3 bench_traffic.py --backward-util DIR_U profiles", "",
+             "Kernel source hash: backward %s" % bench.source_hash(
+                 [os.path.join(bench._CSRC, "kda_bwd.hip"), os.path.join(bench._CSRC, "kda_internal.h")]), "",
+             "| figure | value |", "|---|---|",
+             "| GPU active cycles per launch (GRBM_GUI_ACTIVE / %d XCDs) | %.4g |" % (xcds, active),
+             "| active cycles per chunk | %.0f |" % (active / chunks),
+             "| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (active x %d SIMDs)) | %.1f%% |" % (
+                 cus * simds_per_cu, 100.0 * m["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * cus * simds_per_cu)),
+             "| VALU busy (SQ_ACTIVE_INST_VALU / (active x %d CUs)) | %.1f%% |" % (
+                 cus, 100.0 * m["SQ_ACTIVE_INST_VALU"] / (active * cus)),
+             "| vector instructions per chunk and SIMD (SQ_INSTS_VALU, MFMA included) | %.0f |" % per_chunk_simd("SQ_INSTS_VALU"),
+             "| of which MFMA (SQ_INSTS_MFMA; fp32 16x16x4, 32 cycles each) | %.0f (%.0f cycles) |" % (mfma, 32 * mfma),
+             "| of which fp32 transcendental (SQ_INSTS_VALU_TRANS_F32) | %.0f |" % per_chunk_simd("SQ_INSTS_VALU_TRANS_F32"),
+             "| scalar instructions per chunk and SIMD (SQ_INSTS_SALU) | %.0f |" % per_chunk_simd("SQ_INSTS_SALU"),
+             "| LDS instructions per chunk and SIMD (SQ_INSTS_LDS) | %.0f |" % per_chunk_simd("SQ_INSTS_LDS"),
+             "", "Per chunk and SIMD: counts divided by 256 work-groups x 4 SIMDs x 256 chunks (launch "
+             "prologue and epilogue included)."]
+    os.makedirs(out, exist_ok=True)
+    with open(os.path.join(out, "kda_bwd_b4_h16_t4096_util.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
+    if len(sys.argv) == 4 and sys.argv[1] == "--backward-util":
+        backward_utilisation(sys.argv[2], sys.argv[3])
+        sys.exit(0)
     if len(sys.argv) == 4 and sys.argv[1] == "--util":
         utilisation(sys.argv[2], sys.argv[3])
         sys.exit(0)
