@@ -547,14 +547,15 @@ __global__ __launch_bounds__(512) void bwd_col_kernel(BwdArgs a) {
 // and so is the diagonal of P, whose pair has no decay factor at all: the
 // products take dP without its diagonal, and the diagonal adds dP_tt k_t to
 // dq_t and dP_tt q_t to dk_t directly.
-// One work-group per (b, h, 32-column slice), four waves.  The columns of S
+// One work-group per (b, h, 32-column slice), eight waves.  The columns of S
 // and dS are independent, so dS0, dZ and the slice's dv and dh0 are exact per
 // slice; everything that sums over columns (dM, dP, the three d?b products
 // and the gamma_C term) is linear in this slice's part, so each slice forms
 // its share of dq, dk, dg and dbeta, and a second kernel sums the slices in a
 // fixed order.  Every product is a 16 x 16 output tile of fp32 matrix-core
 // instructions (16x16x4) with operands read from LDS; the phases of a chunk
-// are separated by work-group barriers.
+// are separated by work-group barriers.  Waves w and w + 4 share a SIMD, so
+// one wave's LDS and matrix-core latencies overlap the other's work.
 
 using f32x4 = float __attribute__((ext_vector_type(4)));
 
@@ -624,15 +625,16 @@ __device__ __forceinline__ void bwd_pivots(float &x, const float (&nar)[16]) {
 }
 
 // The inputs of one chunk for thread tid (wave w = tid / 64, lane l), in
-// registers: token l % 16, channels 32 w + 8 (l / 16) .. + 7 of q, k (bf16)
-// and g, so that each 16-lane row holds all 16 tokens of its 8 channels; v of
+// registers: token l % 16, channels 16 w + 4 (l / 16) .. + 3 of q, k (bf16)
+// and g, so that each 16-lane row holds all 16 tokens of its 4 channels; v of
 // the slice (token (tid % 64) / 4, columns 8 (tid % 4) ..); dO of the slice
 // (with d = (tid - 64) % 128: token d / 8, columns 4 (d % 8) ..); the state
-// before the chunk, rows tid / 8 + 32 m, columns 4 (tid % 8) ..; beta of
-// token tid % 16.
+// before the chunk, rows tid / 8 and tid / 8 + 64, columns 4 (tid % 8) ..;
+// beta of token tid % 16.
 struct ChunkIn {
-    uint4 q, k, v;
-    float4 g0, g1, dO, s00, s01, s02, s03;
+    uint2 q, k;
+    uint4 v;
+    float4 g, dO, s00, s01;
     float beta;
 };
 
@@ -653,6 +655,10 @@ __device__ __forceinline__ uint4 ld16(Rsrc r, uint32_t off) {
     const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     return make_uint4(x[0], x[1], x[2], x[3]);
 }
+__device__ __forceinline__ uint2 ld8(Rsrc r, uint32_t off) {
+    const uint32_t __attribute__((ext_vector_type(2))) x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(x[0], x[1]);
+}
 __device__ __forceinline__ float4 ld16f(Rsrc r, uint32_t off) {
     const uint4 x = ld16(r, off);
     return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w));
@@ -670,7 +676,7 @@ __device__ __forceinline__ ChunkIn load_chunk_inputs(const BwdArgs &a, int64_t t
                                                      const float *s0, int64_t sb, int tid) {
     constexpr int D = 128;
     const uint32_t H = static_cast<uint32_t>(a.H), HD = H * D, last = static_cast<uint32_t>(nt - 1) * HD;
-    const uint32_t off = static_cast<uint32_t>(tid & 15) * HD + 32 * (tid >> 6) + 8 * ((tid >> 4) & 3);  // elements
+    const uint32_t off = static_cast<uint32_t>(tid & 15) * HD + 16 * (tid >> 6) + 4 * ((tid >> 4) & 3);  // elements
     const Rsrc rq = buf(static_cast<const uint16_t *>(a.q) + tok0 * D, 2 * (last + D));
     const Rsrc rk = buf(static_cast<const uint16_t *>(a.k) + tok0 * D, 2 * (last + D));
     const Rsrc rg = buf(a.g + tok0 * D, 4 * (last + D));
@@ -679,10 +685,9 @@ __device__ __forceinline__ ChunkIn load_chunk_inputs(const BwdArgs &a, int64_t t
     const Rsrc rs = buf(s0 ? s0 + sb + col0 : nullptr, s0 ? 4u * (127 * D + 32) : 0u);
     const Rsrc rb = buf(a.beta + tok0, 4 * (static_cast<uint32_t>(nt - 1) * H + 1));
     ChunkIn in;
-    in.q = ld16(rq, 2 * off);
-    in.k = ld16(rk, 2 * off);
-    in.g0 = ld16f(rg, 4 * off);
-    in.g1 = ld16f(rg, 4 * off + 16);
+    in.q = ld8(rq, 2 * off);
+    in.k = ld8(rk, 2 * off);
+    in.g = ld16f(rg, 4 * off);
     // (v is stored by threads 0..63 and dO by threads 64..191, each thread the
     // piece it loads; the others load a piece too, to keep the loads free of
     // branches)
@@ -691,9 +696,7 @@ __device__ __forceinline__ ChunkIn load_chunk_inputs(const BwdArgs &a, int64_t t
     in.dO = ld16f(rd, 4 * (static_cast<uint32_t>(l2 >> 3) * HD + 4 * (l2 & 7)));
     const uint32_t so = 4 * (static_cast<uint32_t>(tid >> 3) * D + 4 * (tid & 7));
     in.s00 = ld16f(rs, so);
-    in.s01 = ld16f(rs, so + 4 * 32 * D);
-    in.s02 = ld16f(rs, so + 4 * 64 * D);
-    in.s03 = ld16f(rs, so + 4 * 96 * D);
+    in.s01 = ld16f(rs, so + 4 * 64 * D);
     in.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, 4 * (static_cast<uint32_t>(tid & 15) * H), 0, 0));
     return in;
 }
@@ -724,8 +727,8 @@ __device__ __forceinline__ void store_chunk_inputs(const ChunkIn &in, int nt, in
                                                    float (*sEgi)[P], float (*sV)[PS], float (*sDO)[PS],
                                                    float (*sS0)[PS], float (*sS0T)[P], float *sBeta) {
     {
-        const int t = tid & 15, c0 = 32 * (tid >> 6) + 8 * ((tid >> 4) & 3);
-        float gam[8] = {in.g0.x, in.g0.y, in.g0.z, in.g0.w, in.g1.x, in.g1.y, in.g1.z, in.g1.w};
+        const int t = tid & 15, c0 = 16 * (tid >> 6) + 4 * ((tid >> 4) & 3);
+        float gam[4] = {in.g.x, in.g.y, in.g.z, in.g.w};
         // prefix sums over the 16 tokens of the row, summed in token order:
         // fifteen rounds of "the previous lane's sum plus my g" (the lane before
         // the row's start reads 0) leave lane t with ((g_0 + g_1) + ...) + g_t.
@@ -735,17 +738,17 @@ __device__ __forceinline__ void store_chunk_inputs(const ChunkIn &in, int nt, in
         // log-depth scan the largest dg error on the B=4 H=16 T=4096 workload
         // was 2.8 times as large)
         {
-            const float g0[8] = {gam[0], gam[1], gam[2], gam[3], gam[4], gam[5], gam[6], gam[7]};
+            const float g0[4] = {gam[0], gam[1], gam[2], gam[3]};
 #pragma unroll
             for (int st = 1; st < 16; ++st) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) gam[j] = dpp_mv<0x111>(gam[j]) + g0[j];  // row_shr:1
+                for (int j = 0; j < 4; ++j) gam[j] = dpp_mv<0x111>(gam[j]) + g0[j];  // row_shr:1
             }
         }
-        const uint32_t qw[4] = {in.q.x, in.q.y, in.q.z, in.q.w}, kw[4] = {in.k.x, in.k.y, in.k.z, in.k.w};
-        float qb[8], kb[8], kh[8], eg[8], egi[8];
+        const uint32_t qw[2] = {in.q.x, in.q.y}, kw[2] = {in.k.x, in.k.y};
+        f32x4 qb, kb, kh, eg, egi;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             const float e = __expf(gam[j]), ei = __expf(-gam[j]);
             const float qv = (j & 1) ? bf_hi(qw[j >> 1]) : bf_lo(qw[j >> 1]);
             const float kv = (j & 1) ? bf_hi(kw[j >> 1]) : bf_lo(kw[j >> 1]);
@@ -755,16 +758,11 @@ __device__ __forceinline__ void store_chunk_inputs(const ChunkIn &in, int nt, in
             eg[j] = e;
             egi[j] = ei;
         }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int c = c0 + 4 * h;
-            *reinterpret_cast<f32x4 *>(&sQb[t][c]) = f32x4{qb[4 * h], qb[4 * h + 1], qb[4 * h + 2], qb[4 * h + 3]};
-            *reinterpret_cast<f32x4 *>(&sKb[t][c]) = f32x4{kb[4 * h], kb[4 * h + 1], kb[4 * h + 2], kb[4 * h + 3]};
-            *reinterpret_cast<f32x4 *>(&sKh[t][c]) = f32x4{kh[4 * h], kh[4 * h + 1], kh[4 * h + 2], kh[4 * h + 3]};
-            *reinterpret_cast<f32x4 *>(&sEg[t][c]) = f32x4{eg[4 * h], eg[4 * h + 1], eg[4 * h + 2], eg[4 * h + 3]};
-            *reinterpret_cast<f32x4 *>(&sEgi[t][c]) =
-                f32x4{egi[4 * h], egi[4 * h + 1], egi[4 * h + 2], egi[4 * h + 3]};
-        }
+        *reinterpret_cast<f32x4 *>(&sQb[t][c0]) = qb;
+        *reinterpret_cast<f32x4 *>(&sKb[t][c0]) = kb;
+        *reinterpret_cast<f32x4 *>(&sKh[t][c0]) = kh;
+        *reinterpret_cast<f32x4 *>(&sEg[t][c0]) = eg;
+        *reinterpret_cast<f32x4 *>(&sEgi[t][c0]) = egi;
     }
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (wv == 0) {
@@ -788,9 +786,7 @@ __device__ __forceinline__ void store_chunk_inputs(const ChunkIn &in, int nt, in
     }
     const int r0 = tid >> 3, j = 4 * (tid & 7);
     put_row4(sS0, sS0T, r0, j, in.s00);
-    put_row4(sS0, sS0T, r0 + 32, j, in.s01);
-    put_row4(sS0, sS0T, r0 + 64, j, in.s02);
-    put_row4(sS0, sS0T, r0 + 96, j, in.s03);
+    put_row4(sS0, sS0T, r0 + 64, j, in.s01);
     if (tid < 16) sBeta[tid] = tid < nt ? in.beta : 0.f;
 }
 
@@ -806,7 +802,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // bf16 inputs (fp32 inputs take the token-serial kernel).
-__global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     constexpr int D = 128, kCW = 32, kNS = D / kCW, kC = 16;
     constexpr int kP = 132;  // pitch of the token x channel arrays
     constexpr int kPS = 36;  // pitch of the channel x column and token x column arrays
@@ -814,7 +810,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     __shared__ float sQb[kC][kP], sKb[kC][kP], sKh[kC][kP], sEg[kC][kP], sEgi[kC][kP], sDgam[kC][kP], sW[kC][kP];
     __shared__ float sS0[D][kPS], sG[D][kPS];
     __shared__ float sS0T[kCW][kP], sGT[kCW][kP];  // transposed copies: column j, channel c
-    __shared__ float sV[kC][kPS], sDO[kC][kPS], sZ[kC][kPS], sU[kC][kPS], sdU[2][kC][kPS], sdZ[kC][kPS];
+    __shared__ float sV[kC][kPS], sDO[kC][kPS], sZ[kC][kPS], sU[kC][kPS], sdU[4][kC][kPS], sdZ[kC][kPS];
     __shared__ float sA[kC][kP16], sGr[kC][kP16], sPs[kC][kP16], sN[kC][kP16], sM[kC][kP16];
     __shared__ float sdP[kC][kP16], sdGr[kC][kP16];
     __shared__ float sBeta[kC], sDgC[D], sDB[kC], sDPd[kC];
@@ -823,7 +819,10 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     const int slice = static_cast<int>(blockIdx.x % kNS);
     const int64_t b = bh / a.H, h = bh % a.H;
     const int tid_k = threadIdx.x, tid = tid_k, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(tid_k >> 6);  // wave-uniform: its branches and offsets are scalar
+    // wave-uniform: its branches and offsets are scalar.  Wave w owns row
+    // block w of dS (channels 16 w .. 16 w + 15, both column tiles) and
+    // channel block w of the d?b products.
+    const int w = __builtin_amdgcn_readfirstlane(tid_k >> 6);
     const int64_t T = a.T, H = a.H;
     const int col0 = slice * kCW;
     float *part = a.part + static_cast<int64_t>(slice) * a.part_stride;
@@ -832,15 +831,14 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     const uint32_t HD = static_cast<uint32_t>(a.H) * D;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-    // dS, this wave's four tiles of the 128 x 32 slice: tile q is row block
-    // 2 w + q / 2, column tile q % 2; component i is row 4 g4 + i of the block
-    f32x4 dS[4];
+    // dS, this wave's two tiles of the 128 x 32 slice: tile ct is row block w,
+    // column tile ct; component i is row 4 g4 + i of the block
+    f32x4 dS[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int rb = 2 * w + (q >> 1), ct = q & 1;
+    for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            dS[q][i] = a.dhT ? a.dhT[sb + (16 * rb + 4 * g4 + i) * D + col0 + 16 * ct + r16] : 0.f;
+            dS[ct][i] = a.dhT ? a.dhT[sb + (16 * w + 4 * g4 + i) * D + col0 + 16 * ct + r16] : 0.f;
     }
     // (dS has landed before the loop: without this wait the loop would wait for
     // every outstanding store, once per chunk, where it first scales dS)
@@ -879,7 +877,10 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
         //     Qb, Kb, Kh are formed on the way (e^gamma_C is row 15 of sEg)
         store_chunk_inputs(in, nt, tid, sQb, sKb, sKh, sEg, sEgi, sV, sDO, sS0, sS0T, sBeta);
         lds_barrier();
-        // (F1) Kb Kh^T and A (wave 0), scale P (wave 1), Z = V - Kb S0 (waves 2, 3)
+        // (F1) Kb Kh^T and A (wave 0), scale P (wave 1), Z = V - Kb S0 (waves 2,
+        // 3); waves 4 .. 7 start their dQb tiles: dO S0^T (transposed: channel
+        // block w as rows).  Waves 0 .. 3 start theirs in F3.
+        f32x4 accQ = zero, accKb, accKh;
         if (w == 0) {
             const f32x4 gr = tile_mm_kc<D>(&sKb[0][0], kP, &sKh[0][0], kP, zero, lane);
 #pragma unroll
@@ -895,7 +896,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
                 const int r = 4 * g4 + i;
                 sPs[r][r16] = r16 <= r ? a.scale * pr[i] : 0.f;
             }
-        } else {
+        } else if (w < 4) {
             const int ct = w - 2;
             const f32x4 x = tile_mm_kc<D>(&sKb[0][0], kP, &sS0T[16 * ct][0], kP, zero, lane);
 #pragma unroll
@@ -903,11 +904,14 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
                 const int t = 4 * g4 + i;
                 sZ[t][16 * ct + r16] = sV[t][16 * ct + r16] - x[i];
             }
+        } else {
+            accQ = tile_mm_kc<kCW>(&sS0[16 * w][0], kPS, &sDO[0][0], kPS, zero, lane);
         }
         lds_barrier();
 
-        // (F2) N = (I + A)^-1 and M = N diag(beta): row group g4 of wave w solves column 4 w + g4
-        {
+        // (F2) N = (I + A)^-1 and M = N diag(beta): row group g4 of wave w < 4
+        // solves column 4 w + g4
+        if (w < 4) {
             float nar[kC];
 #pragma unroll
             for (int u = 0; u < kC; ++u) nar[u] = -sA[r16][u];
@@ -919,63 +923,51 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
         }
         lds_barrier();
 
-        // (F3) U = M Z (waves 0, 1); every wave starts its dQb tiles, dO S0^T
-        // (transposed: this wave's channel blocks cb = 2 w + e as rows)
+        // (F3) U = M Z (waves 0, 1); waves 0 .. 3 start their dQb tiles
         if (w < 2) {
             const f32x4 uu = tile_mm<kC>(&sM[0][0], kP16, 1, &sZ[0][16 * w], kPS, 1, zero, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sU[4 * g4 + i][16 * w + r16] = uu[i];
         }
-        f32x4 accQ[2], accKb[2], accKh[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-            accQ[e] = tile_mm_kc<kCW>(&sS0[16 * (2 * w + e)][0], kPS, &sDO[0][0], kPS, zero, lane);
+        if (w < 4) accQ = tile_mm_kc<kCW>(&sS0[16 * w][0], kPS, &sDO[0][0], kPS, zero, lane);
 
         // (F4) G = D_C dS (kept in dS and written for the products) and the
         // gamma_C term of D_C S0: rowsum(S0 .* G)
         {
-            float dgc[2][4];
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dgc[e][i] = 0.f;
+            f32x4 dgc = zero;
             // (rows 4 g4 .. 4 g4 + 3 of a tile are consecutive in sEg's last row,
             // in sS0T and in sGT: one 16-byte access each)
+            const int row0 = 16 * w + 4 * g4;
+            const f32x4 egc = *reinterpret_cast<const f32x4 *>(&sEg[kC - 1][row0]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int rb = 2 * w + (q >> 1), ct = q & 1, row0 = 16 * rb + 4 * g4, col = 16 * ct + r16;
+            for (int ct = 0; ct < 2; ++ct) {
+                const int col = 16 * ct + r16;
                 const f32x4 s0 = *reinterpret_cast<const f32x4 *>(&sS0T[col][row0]);
-                dS[q] *= *reinterpret_cast<const f32x4 *>(&sEg[kC - 1][row0]);
+                dS[ct] *= egc;
+                dgc += s0 * dS[ct];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    dgc[q >> 1][i] += s0[i] * dS[q][i];
-                    sG[row0 + i][col] = dS[q][i];
-                }
-                *reinterpret_cast<f32x4 *>(&sGT[col][row0]) = dS[q];
+                for (int i = 0; i < 4; ++i) sG[row0 + i][col] = dS[ct][i];
+                *reinterpret_cast<f32x4 *>(&sGT[col][row0]) = dS[ct];
             }
 #pragma unroll
-            for (int e = 0; e < 2; ++e)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float v = row_sum16(dgc[e][i]);
-                    if (r16 == 0) sDgC[16 * (2 * w + e) + 4 * g4 + i] = v;
-                }
+            for (int i = 0; i < 4; ++i) {
+                const float v = row_sum16(dgc[i]);
+                if (r16 == 0) sDgC[row0 + i] = v;
+            }
         }
         lds_barrier();
 
-        // (B1) dU = Kh G + scale P^T dO in two channel halves (wave w: column
-        // tile w % 2, half w / 2); dKh starts as U G^T; wave 3 forms dP
+        // (B1) dU = Kh G + scale P^T dO in four channel quarters (wave w: column
+        // tile w % 2, quarter w / 2); dKh starts as U G^T; wave 7 forms dP
         {
-            const int ct = w & 1, kh = w >> 1;
-            f32x4 du = tile_mm_kc<64>(&sKh[0][64 * kh], kP, &sGT[16 * ct][64 * kh], kP, zero, lane);
-            if (kh == 0) du = tile_mm<kC>(&sPs[0][0], 1, kP16, &sDO[0][16 * ct], kPS, 1, du, lane);
+            const int ct = w & 1, kq = w >> 1;
+            f32x4 du = tile_mm_kc<32>(&sKh[0][32 * kq], kP, &sGT[16 * ct][32 * kq], kP, zero, lane);
+            if (kq == 0) du = tile_mm<kC>(&sPs[0][0], 1, kP16, &sDO[0][16 * ct], kPS, 1, du, lane);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sdU[kh][4 * g4 + i][16 * ct + r16] = du[i];
+            for (int i = 0; i < 4; ++i) sdU[kq][4 * g4 + i][16 * ct + r16] = du[i];
         }
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-            accKh[e] = tile_mm_kc<kCW>(&sG[16 * (2 * w + e)][0], kPS, &sU[0][0], kPS, zero, lane);
-        if (w == 3) {
+        accKh = tile_mm_kc<kCW>(&sG[16 * w][0], kPS, &sU[0][0], kPS, zero, lane);
+        if (w == 7) {
             const f32x4 dp = tile_mm_kc<kCW>(&sDO[0][0], kPS, &sU[0][0], kPS, zero, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -987,14 +979,14 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
         lds_barrier();
 
         // (B2) dZ = M^T dU (waves 0, 1; it is dv); dM = dU Z^T and the solve's
-        // adjoint (wave 3)
+        // adjoint (wave 3).  dU is the sum of B1's four quarters.
         if (w < 2) {
             const int ct = w;
             f32x4 dz = zero;
 #pragma unroll
             for (int k0 = 0; k0 < kC; k0 += 4) {
-                const int k = k0 + g4;
-                dz = mfma4(sM[k][r16], sdU[0][k][16 * ct + r16] + sdU[1][k][16 * ct + r16], dz);
+                const int k = k0 + g4, c = 16 * ct + r16;
+                dz = mfma4(sM[k][r16], (sdU[0][k][c] + sdU[1][k][c]) + (sdU[2][k][c] + sdU[3][k][c]), dz);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1013,7 +1005,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
             for (int k0 = 0; k0 < kCW; k0 += 4) {
                 const int k = k0 + g4;
-                dmt = mfma4(sZ[r16][k], sdU[0][r16][k] + sdU[1][r16][k], dmt);
+                dmt = mfma4(sZ[r16][k], (sdU[0][r16][k] + sdU[1][r16][k]) + (sdU[2][r16][k] + sdU[3][r16][k]), dmt);
             }
             f32x4 t1 = zero;  // T1(4 g4 + i, r16) = sum_s dM(4 g4 + i, s) beta_s N(r16, s)
 #pragma unroll
@@ -1048,29 +1040,24 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
         // (B3) dS0 = G - Kb^T dZ + scale Qb^T dO (this wave's tiles: the next
         // dS); dKb starts as -dZ S0^T
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int rb = 2 * w + (q >> 1), ct = q & 1;
-            const f32x4 t1 = tile_mm<kC>(&sKb[0][16 * rb], 1, kP, &sdZ[0][16 * ct], kPS, 1, zero, lane);
-            const f32x4 t2 = tile_mm<kC>(&sQb[0][16 * rb], 1, kP, &sDO[0][16 * ct], kPS, 1, zero, lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dS[q][i] = (dS[q][i] - t1[i]) + a.scale * t2[i];
+        for (int ct = 0; ct < 2; ++ct) {
+            const f32x4 t1 = tile_mm<kC>(&sKb[0][16 * w], 1, kP, &sdZ[0][16 * ct], kPS, 1, zero, lane);
+            const f32x4 t2 = tile_mm<kC>(&sQb[0][16 * w], 1, kP, &sDO[0][16 * ct], kPS, 1, zero, lane);
+            dS[ct] = (dS[ct] - t1) + a.scale * t2;
         }
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-            accKb[e] = tile_mm_kc<kCW>(&sS0[16 * (2 * w + e)][0], kPS, &sdZ[0][0], kPS, zero, lane);
+        accKb = tile_mm_kc<kCW>(&sS0[16 * w][0], kPS, &sdZ[0][0], kPS, zero, lane);
         // (B3 writes no LDS: B4 follows without a barrier)
 
-        // (B4) finish dQb, dKb, dKh on this wave's channel blocks; dq, dk and
-        // dgamma of its 16 tokens x 32 channels.  The tiles are transposed
+        // (B4) finish dQb, dKb, dKh on this wave's channel block; dq, dk and
+        // dgamma of its 16 tokens x 16 channels.  The tiles are transposed
         // (channel rows, token columns; the accumulators above likewise), so
         // lane (r16, g4) holds channels 4 g4 .. 4 g4 + 3 of token r16: its LDS
         // reads and writes and its partial stores are 16 bytes each.
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int cb = 2 * w + e;
-            f32x4 dqb = a.scale * accQ[e];
+        {
+            const int cb = w;
+            f32x4 dqb = a.scale * accQ;
             dqb = tile_mm<kC>(&sKh[0][16 * cb], 1, kP, &sdP[0][0], 1, kP16, dqb, lane);
-            f32x4 dkb = -accKb[e];
+            f32x4 dkb = -accKb;
             dkb = tile_mm<kC>(&sKh[0][16 * cb], 1, kP, &sdGr[0][0], 1, kP16, dkb, lane);
             // the pairs' part of dKh on its own (the U G^T part is W, summed apart)
             f32x4 dkh = tile_mm<kC>(&sKb[0][16 * cb], 1, kP, &sdGr[0][0], kP16, 1, zero, lane);
@@ -1083,64 +1070,54 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
             const f32x4 kb = *reinterpret_cast<const f32x4 *>(&sKb[t][c]);
             const float dpd = sDPd[t];
             *reinterpret_cast<f32x4 *>(&sDgam[t][c]) = (dqb * qb + dkb * kb) - dkh * kh;
-            *reinterpret_cast<f32x4 *>(&sW[t][c]) = accKh[e] * kh;
+            *reinterpret_cast<f32x4 *>(&sW[t][c]) = accKh * kh;
             const uint32_t o = 4 * (static_cast<uint32_t>(t) * HD + c);
-            st16(pq, o, dqb * eg + dpd * (kb * egi));                            // + dP_tt k_t
-            st16(pk, o, (dkb * eg + (accKh[e] + dkh) * egi) + dpd * (qb * egi));  // + dP_tt q_t
+            st16(pq, o, dqb * eg + dpd * (kb * egi));                        // + dP_tt k_t
+            st16(pk, o, (dkb * eg + (accKh + dkh) * egi) + dpd * (qb * egi));  // + dP_tt q_t
         }
         lds_barrier();
 
         // dg: the suffix sums of dgamma over the chunk, the gamma_C term and the
         // prefix sums of W (all before token t), as scans across the 16 lanes
         // of a row: lane (t = tid % 16) of row j of wave w holds token t of
-        // channels 32 w + 8 j .. + 7 (lanes past the row's end read 0).  And
+        // channels 16 w + 4 j .. + 3 (lanes past the row's end read 0).  And
         // this slice's share of dbeta.
         {
-            const int t = tid & 15, c0 = 32 * w + 8 * ((tid >> 4) & 3);
-            float x[8], y[8];
+            const int t = tid & 15, c0 = 16 * w + 4 * ((tid >> 4) & 3);
+            f32x4 x = *reinterpret_cast<const f32x4 *>(&sDgam[t][c0]);
+            const f32x4 ww = *reinterpret_cast<const f32x4 *>(&sW[t][c0]);
+            f32x4 y;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const f32x4 d = *reinterpret_cast<const f32x4 *>(&sDgam[t][c0 + 4 * h]);
-                const f32x4 ww = *reinterpret_cast<const f32x4 *>(&sW[t][c0 + 4 * h]);
+            for (int i = 0; i < 4; ++i) y[i] = dpp_mv<0x111>(ww[i]);  // row_shr:1: W of token t - 1
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    x[4 * h + i] = d[i];
-                    y[4 * h + i] = dpp_mv<0x111>(ww[i]);  // row_shr:1: W of token t - 1
-                }
-            }
+            for (int i = 0; i < 4; ++i) x[i] += dpp_mv<0x101>(x[i]);  // row_shl:1
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] += dpp_mv<0x101>(x[j]);  // row_shl:1
+            for (int i = 0; i < 4; ++i) y[i] += dpp_mv<0x111>(y[i]);  // row_shr:1
 #pragma unroll
-            for (int j = 0; j < 8; ++j) y[j] += dpp_mv<0x111>(y[j]);  // row_shr:1
+            for (int i = 0; i < 4; ++i) x[i] += dpp_mv<0x102>(x[i]);  // row_shl:2
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] += dpp_mv<0x102>(x[j]);  // row_shl:2
+            for (int i = 0; i < 4; ++i) y[i] += dpp_mv<0x112>(y[i]);  // row_shr:2
 #pragma unroll
-            for (int j = 0; j < 8; ++j) y[j] += dpp_mv<0x112>(y[j]);  // row_shr:2
+            for (int i = 0; i < 4; ++i) x[i] += dpp_mv<0x104>(x[i]);  // row_shl:4
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] += dpp_mv<0x104>(x[j]);  // row_shl:4
+            for (int i = 0; i < 4; ++i) y[i] += dpp_mv<0x114>(y[i]);  // row_shr:4
 #pragma unroll
-            for (int j = 0; j < 8; ++j) y[j] += dpp_mv<0x114>(y[j]);  // row_shr:4
+            for (int i = 0; i < 4; ++i) x[i] += dpp_mv<0x108>(x[i]);  // row_shl:8
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] += dpp_mv<0x108>(x[j]);  // row_shl:8
+            for (int i = 0; i < 4; ++i) y[i] += dpp_mv<0x118>(y[i]);  // row_shr:8
+            f32x4 dg;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) y[j] += dpp_mv<0x118>(y[j]);  // row_shr:8
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                f32x4 dg;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dg[i] = (x[4 * h + i] + sDgC[c0 + 4 * h + i]) + y[4 * h + i];
-                st16(pg, 4 * (static_cast<uint32_t>(t) * HD + c0 + 4 * h), dg);
-            }
+            for (int i = 0; i < 4; ++i) dg[i] = (x[i] + sDgC[c0 + i]) + y[i];
+            st16(pg, 4 * (static_cast<uint32_t>(t) * HD + c0), dg);
             if (tid < kC) st4(pb, 4 * (static_cast<uint32_t>(tid) * static_cast<uint32_t>(H)), sDB[tid]);
         }
     }
 
     if (a.dh0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int rb = 2 * w + (q >> 1), ct = q & 1;
+        for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a.dh0[sb + (16 * rb + 4 * g4 + i) * D + col0 + 16 * ct + r16] = dS[q][i];
+            for (int i = 0; i < 4; ++i) a.dh0[sb + (16 * w + 4 * g4 + i) * D + col0 + 16 * ct + r16] = dS[ct][i];
         }
     }
 }
@@ -1183,7 +1160,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
         // of accuracy (relative to its rms) under strong decay or beta = 1.
         // (the chunk kernel's 32-bit byte offsets need 16 H D 4 < 2^31)
         const dim3 grid(static_cast<unsigned>(BH * 4));
-        if (a.bf16 && a.H < 65536) hipLaunchKernelGGL(bwd_chunk_kernel, grid, dim3(256), 0, s, a);
+        if (a.bf16 && a.H < 65536) hipLaunchKernelGGL(bwd_chunk_kernel, grid, dim3(512), 0, s, a);
         else if (a.bf16) hipLaunchKernelGGL((bwd_col_kernel<true>), grid, dim3(512), 0, s, a);
         else hipLaunchKernelGGL((bwd_col_kernel<false>), grid, dim3(512), 0, s, a);
     } else if (a.D == 16) {
