@@ -15,8 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_prefill_valu.hip", "kda_prefill_mfma.hip", "kda_prefill_mfma_gate.hip", "kda_decode.hip",
-           "kda_kcp.hip", "kda_bwd.hip"]
+SOURCES = ["kda_api.cpp", "kda_prefill_valu.hip", "kda_prefill_mfma.hip", "kda_prefill_mfma_gate.hip",
+           "kda_prefill_f32.hip", "kda_decode.hip", "kda_kcp.hip", "kda_bwd.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

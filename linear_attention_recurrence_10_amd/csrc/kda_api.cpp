@@ -131,6 +131,8 @@ namespace {
 
 kda_status launch_prefill(const kda::PrefillArgs &a, hipStream_t s) {
     if (kda::prefill_mfma_supported(a)) return launch_status(kda::launch_prefill_mfma(a, s), "kda prefill (mfma)");
+    if (kda::prefill_f32_supported(a) && !kda::prefill_mfma_disabled())
+        return launch_status(kda::launch_prefill_f32(a, s), "kda prefill (fp32 mfma)");
     return launch_status(kda::launch_prefill_valu(a, s), "kda prefill (valu)");
 }
 

@@ -72,6 +72,12 @@ hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_mfma_gate(const PrefillArgs &a, dim3 grid, hipStream_t s);  // gate-logit variants
 bool prefill_mfma_supported(const PrefillArgs &a);
+// fp32 inputs at d = 128 on the fp32 matrix cores (kda_prefill_f32.hip)
+hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t s);
+bool prefill_f32_supported(const PrefillArgs &a);
+// KDA_DISABLE_MFMA=1 in the environment (read once per process) routes every
+// prefill to the fp32 vector-ALU kernel: a comparison knob for tests
+bool prefill_mfma_disabled();
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 // Segmented prefill helpers (kda_kcp.hip).
 // The fixed per-device workspace of kda_chunk_fwd_kcp_noalloc: 32 MiB, room

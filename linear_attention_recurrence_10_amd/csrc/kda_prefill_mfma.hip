@@ -16,6 +16,8 @@ static const bool g_mfma_disabled = [] {
     return env && env[0] == '1';
 }();
 
+bool prefill_mfma_disabled() { return g_mfma_disabled; }
+
 bool prefill_mfma_supported(const PrefillArgs &a) {
     // the kernel's 32-bit in-chunk byte offsets need kC * H * 128 * 4 < 2^31,
     // i.e. H < 65536 (the products are formed in 32 bits)

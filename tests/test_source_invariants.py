@@ -105,7 +105,8 @@ def test_instruction_asm_only_in_solver_helpers():
     body = function_body(text, "solve")
     assert not re.search(r"\b(mfma16|mfma32|mm16|mm32|__builtin_amdgcn_mfma\w*)\s*\(", body)
     # the other kernels issue no instruction from inline assembly
-    for name in ("kda_bwd.hip", "kda_decode.hip", "kda_kcp.hip", "kda_prefill_valu.hip"):
+    for name in ("kda_bwd.hip", "kda_f32mfma.h", "kda_prefill_f32.hip", "kda_decode.hip", "kda_kcp.hip",
+                 "kda_prefill_valu.hip"):
         assert not asm_statements(source(name)), name
 
 
