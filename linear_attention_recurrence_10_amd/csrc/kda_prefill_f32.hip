@@ -62,6 +62,21 @@ __device__ __forceinline__ F32In load_f32_inputs(const PrefillArgs &a, int64_t t
     return in;
 }
 
+// e^x as 2^(x log2 e) on the hardware exp2, with the rounding of the product
+// carried separately: x log2 e = yh + yl, where yh is the fp32 product, fma
+// gives its exact residual and x (log2 e - c) adds the error of the constant
+// c; then 2^(yh + yl) = 2^yh (1 + yl ln 2) to within yl^2, which is below
+// 2^-40 here (|x| <= 80 + 16 at the floor gate).  Six operations, and the
+// error of the hardware exp2 instead of |x| 2^-24.
+__device__ __forceinline__ float exp_split(float x) {
+    constexpr float kC = 1.44269502162933349609375f;  // log2 e, rounded to fp32
+    constexpr float kCLo = 1.925963001e-8f;           // log2 e - kC
+    constexpr float kLn2 = 0.693147182464599609375f;  // ln 2, rounded to fp32
+    const float yh = x * kC;
+    const float yl = __builtin_fmaf(x, kC, -yh) + x * kCLo;
+    return __builtin_amdgcn_exp2f(yh) * __builtin_fmaf(yl, kLn2, 1.f);
+}
+
 template <int P, int PS>
 struct F32Buf {
     float Qb[kF32C][P], Kb[kF32C][P], Kh[kF32C][P];
@@ -96,7 +111,7 @@ __device__ __forceinline__ void store_f32_inputs(const PrefillArgs &a, const F32
     f32x4 qb, kb, kh, eg;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float e = expf(gam[j]), ei = expf(-gam[j]);
+        const float e = exp_split(gam[j]), ei = exp_split(-gam[j]);
         qb[j] = qv[j] * e;
         kb[j] = kv[j] * e;
         kh[j] = kv[j] * ei;

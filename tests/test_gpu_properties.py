@@ -147,27 +147,29 @@ def test_binding_raises_kda_error():
         kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], o=x["g"].view(1, 32, 2, 128))
 
 
-def test_mfma_and_valu_kernels_agree(tmp_path):
-    """The matrix-core kernel (bf16, d=128) and the fp32 vector kernel compute
-    the same chunk form; both are checked against the oracle elsewhere.  The
-    library reads KDA_DISABLE_MFMA once per process, so the vector kernel runs
-    in a child process on the same seeded inputs."""
+@pytest.mark.parametrize("dtype,tol", [("bf16", 2e-3), ("f32", 2e-5)])
+def test_mfma_and_valu_kernels_agree(tmp_path, dtype, tol):
+    """The matrix-core kernels (bf16 pairs for bf16 inputs, fp32 products for
+    fp32 inputs, d=128) and the fp32 vector kernel compute the same chunk
+    form; all are checked against the oracle elsewhere.  The library reads
+    KDA_DISABLE_MFMA once per process, so the vector kernel runs in a child
+    process on the same seeded inputs."""
     import subprocess
 
-    x = kda_inputs.prefill_inputs(2, 200, 3, 128, "bf16", h0=True, seed=49, device=DEV)
+    x = kda_inputs.prefill_inputs(2, 200, 3, 128, dtype, h0=True, seed=49, device=DEV)
     o1, h1 = fwd(x, x["h0"])
     torch.cuda.synchronize()
     out = str(tmp_path / "valu.pt")
     script = (
         "import sys, torch; sys.path[:0] = %r\n"
         "import kda_inputs, linear_attention_recurrence_10_amd as kda\n"
-        "x = kda_inputs.prefill_inputs(2, 200, 3, 128, 'bf16', h0=True, seed=49, device='cuda:0')\n"
+        "x = kda_inputs.prefill_inputs(2, 200, 3, 128, %r, h0=True, seed=49, device='cuda:0')\n"
         "o, h = kda.chunk_fwd(x['q'], x['k'], x['v'], x['g'], x['beta'], x['h0'])\n"
         "torch.cuda.synchronize()\n"
-        "torch.save({'o': o.cpu(), 'h': h.cpu()}, %r)\n" % ([ROOT, HERE], out))
+        "torch.save({'o': o.cpu(), 'h': h.cpu()}, %r)\n" % ([ROOT, HERE], dtype, out))
     env = dict(os.environ, KDA_DISABLE_MFMA="1")
     r = subprocess.run([sys.executable, "-c", script], env=env, timeout=300, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     ref = torch.load(out, weights_only=True)
-    assert rel_err(o1.cpu(), ref["o"]) < 2e-3 and rel_err(h1.cpu(), ref["h"]) < 2e-3
+    assert rel_err(o1.cpu(), ref["o"]) < tol and rel_err(h1.cpu(), ref["h"]) < tol
     assert not torch.equal(o1.cpu(), ref["o"])  # the child really ran the other kernel
