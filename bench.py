@@ -317,6 +317,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--no-qknorm", action="store_true",
                     help="skip timing the prefill and decode step with the fused q/k normalisation")
+    ap.add_argument("--no-f32", action="store_true",
+                    help="skip timing the same prefill workload with fp32 q, k and v (the fp32 matrix-core kernel)")
     ap.add_argument("--no-host-cost", action="store_true",
                     help="skip the host cost per decode call (its small launches would mix into a kernel trace)")
     ap.add_argument("--no-configs", action="store_true",
@@ -463,6 +465,16 @@ def main():
         if d is not None:
             qkn["decode"] = time_launches(torch, stream, lambda: kda.decode_step_qknorm(
                 d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], eps=1e-6, o=od, stream=stream), args.steps)
+    f32 = None
+    if not args.no_f32:
+        # the same workload with fp32 q, k and v: the fp32 matrix-core kernel
+        # (a few launches: each reads 7.5 GB)
+        log("fp32 inputs")
+        xf = kda_inputs.prefill_inputs(cfg.B, cfg.T, cfg.H, cfg.D, "f32", seed=cfg.seed, device=dev)
+        f32 = time_launches(torch, stream, lambda: kda.chunk_fwd(
+            xf["q"], xf["k"], xf["v"], xf["g"], xf["beta"], None, o=o, hT=hT, stream=stream), min(args.steps, 5))
+        del xf
+        torch.cuda.empty_cache()
     seg = None
     if args.segments > 0:
         seg = time_segmented(kda, torch, stream, args.segments, args.steps)
@@ -535,6 +547,15 @@ def main():
             result["qknorm"]["decode"] = {"workload": dcfg.name + "_qknorm", "ms": dq_avg, "min_ms": dq_min,
                                           "achieved": dq_ach, "frac": dq_ach / HBM_PEAK_GBPS,
                                           "alg_bytes_per_launch": dq_bytes, "traffic": load_traffic("decode_qknorm")}
+    if f32 is not None:
+        f_avg, f_min = f32
+        f_bytes = prefill_bytes(cfg.B, cfg.T, cfg.H, cfg.D, 4, h0=False, hT=True)
+        f_ach = f_bytes / (f_avg * 1e-3) / 1e9
+        result["prefill_f32"] = {"workload": cfg.name.replace("bf16", "f32"), "ms": f_avg, "min_ms": f_min,
+                                 "tokens_per_s": tokens / (f_avg * 1e-3), "achieved": f_ach,
+                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": f_ach / HBM_PEAK_GBPS,
+                                 "alg_bytes_per_launch": f_bytes,
+                                 "note": "fp32 q, k, v on the fp32 matrix cores (16x16x4); latency bound"}
     if seg is not None:
         result["segmented"] = seg
     result["copy"] = copy_bandwidth(torch, stream)
