@@ -416,8 +416,8 @@ kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const floa
                          const float *h0, const float *dO, const float *dhT, float *dq, float *dk, float *dv,
                          float *dg, float *dbeta, float *dh0, void *ws, uint64_t ws_bytes, int64_t B, int64_t T,
                          int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale, void *stream) {
-    // the forward arguments are checked as for the prefill (with dq standing in for o: the
-    // checkpoint pass writes its o there, and the gradient overwrites it at the end)
+    // the forward arguments are checked as for the prefill (with dq standing in for o;
+    // the checkpoint pass itself writes no o)
     // (every host-side check comes before the device is queried)
     kda::PrefillArgs fa;
     kda_status st = chunk_fwd(q, k, v, g, kda::kGateLogDecay, 0.f, beta, h0, dq, nullptr, nullptr, 0, B, T, H, Dk, Dv,
@@ -454,10 +454,10 @@ kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const floa
     hipStream_t s = static_cast<hipStream_t>(stream);
     float *ckpt = static_cast<float *>(ws);
     const int64_t n_ck = T / kda::kChunk;
-    // the states after every 16 tokens (o goes to dq, overwritten below)
+    // the states after every 16 tokens (a pass that writes no o)
     if (n_ck > 0) {
         kda::PrefillArgs ca = fa;
-        ca.o = dq;
+        ca.o = nullptr;
         ca.hT = nullptr;
         ca.ckpt = ckpt;
         ca.ckpt_every = 1;

@@ -1,7 +1,8 @@
 // kda_prefill_mfma.hip -- launches of the chunked KDA prefill on the gfx950
 // matrix cores (the kernel template is in kda_prefill_mfma.h): the fp32
 // log-decay gate, with or without state checkpoints or the q/k
-// normalisation, and the passes of the segmented prefill that write no o.
+// normalisation, and the passes that write no o (those of the segmented
+// prefill, and the checkpoint pass of the backward).
 // The gate-logit variants live in kda_prefill_mfma_gate.hip.
 #include <atomic>
 
@@ -35,13 +36,14 @@ hipError_t launch_prefill_mfma(const PrefillArgs &args, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(rounds * 8 * kNV));
     // checkpoints, and the passes without o, come with the fp32 log-decay gate
     // and without the q/k normalisation only (the entry points offer no other
-    // combination)
-    const bool plain = !a.ckpt && a.gate == kGateLogDecay && !a.qk_norm;
-    if ((!a.o || !a.v) && !plain) return hipErrorInvalidValue;
-    if (!a.v && a.o) return hipErrorInvalidValue;
-    if (a.ckpt && (a.gate != kGateLogDecay || a.qk_norm)) return hipErrorInvalidValue;
-    if (a.ckpt)
+    // combination); checkpoints always come with values
+    const bool plain = a.gate == kGateLogDecay && !a.qk_norm;
+    if ((!a.o || !a.v || a.ckpt) && !plain) return hipErrorInvalidValue;
+    if (!a.v && (a.o || a.ckpt)) return hipErrorInvalidValue;
+    if (a.ckpt && a.o)
         hipLaunchKernelGGL((prefill_mfma_kernel<true, kGateLogDecay, kFull>), grid, dim3(kThreads), 0, s, a);
+    else if (a.ckpt)
+        hipLaunchKernelGGL((prefill_mfma_kernel<true, kGateLogDecay, kNoOut>), grid, dim3(kThreads), 0, s, a);
     else if (a.gate != kGateLogDecay)
         return launch_prefill_mfma_gate(a, grid, s);
     else if (a.qk_norm)
