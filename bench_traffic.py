@@ -25,6 +25,9 @@ usage: python3 bench_traffic.py DIR_T DIR_F DIR_W OUT
            backward's chunk kernel: OUT/kda_bwd_b4_h16_t4096_util.md)
        python3 bench_traffic.py --backward DIR_T DIR_F DIR_W OUT   (trace and traffic of
            bench.py --backward-only: OUT/kda_bwd_b4_h16_t4096_rocprof.md)
+       python3 bench_traffic.py --waits prefill|backward DIR_S OUT   (where the waves' cycles
+           go, from one counter run: OUT/kda_prefill_64k_waits.md or
+           OUT/kda_bwd_b4_h16_t4096_waits.md)
 """
 from __future__ import annotations
 
@@ -43,6 +46,8 @@ DECODE = "decode_kernel"
 QKNORM = "prefill_mfma_qknorm_kernel<0>"  # the prefill with the fused q/k normalisation
 DECODE_QKNORM = "decode_qknorm_kernel"
 COPY = "copyBuffer"
+# the backward's chunk kernel and the helpers it includes
+BWD_SOURCES = [os.path.join(bench._CSRC, f) for f in ("kda_bwd.hip", "kda_internal.h", "kda_f32mfma.h")]
 
 
 def _csv(d, suffix):
@@ -240,7 +245,7 @@ def backward(dt, df, dw, out):
     lines = ["# rocprofv3: KDA backward pass (B=4 H=16 T=4096 d=128, bf16 q/k/v, random h0, dO and dhT)", "",
              "Commands (from the repository root):", ""] + ["    " + c for c in cmds] + [
              "", "Kernel source hash: backward %s, prefill %s" % (
-                 bench.source_hash([os.path.join(bench._CSRC, "kda_bwd.hip"), os.path.join(bench._CSRC, "kda_internal.h")]),
+                 bench.source_hash(BWD_SOURCES),
                  bench.source_hash()),
              "", "Copy calibration scale factors %.4f (fetch), %.4f (write)." % (sf, sw), "",
              "| kernel | role | calls | avg us | min us | scaled HBM bytes per launch |", "|---|---|---|---|---|---|"]
@@ -335,8 +340,7 @@ def backward_utilisation(du, out, cus=256, simds_per_cu=4, xcds=8):
     lines = ["# rocprofv3: KDA backward chunk kernel (B=4 H=16 T=4096 d=128) issue and pipe utilisation", "",
              "Commands (from the repository root):", "", "    " + cmd,
              "    python3 bench_traffic.py --backward-util DIR_U profiles", "",
-             "Kernel source hash: backward %s" % bench.source_hash(
-                 [os.path.join(bench._CSRC, "kda_bwd.hip"), os.path.join(bench._CSRC, "kda_internal.h")]), "",
+             "Kernel source hash: backward %s" % bench.source_hash(BWD_SOURCES), "",
              "| figure | value |", "|---|---|",
              "| GPU active cycles per launch (GRBM_GUI_ACTIVE / %d XCDs) | %.4g |" % (xcds, active),
              "| active cycles per chunk | %.0f |" % (active / chunks),
@@ -357,7 +361,73 @@ def backward_utilisation(du, out, cus=256, simds_per_cu=4, xcds=8):
     print("\n".join(lines))
 
 
+WAIT_COUNTERS = ("SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_WAIT_INST_LDS "
+                 "SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_COEXEC_CYCLES GRBM_GUI_ACTIVE")
+
+
+def waits(which, ds, out, xcds=8):
+    """Where the waves' cycles go, from one counter run of WAIT_COUNTERS.
+
+    SQ_WAVE_CYCLES (wave lifetime), SQ_WAIT_ANY (waiting on anything: a
+    dependency, a memory or LDS count, a barrier), SQ_WAIT_INST_ANY (an
+    instruction ready but not yet issued) and SQ_ACTIVE_INST_ANY (issuing)
+    count wave-cycles in units of four cycles, summed over the waves (the
+    three shares add up to the lifetime).  The shares are per wave-cycle, so
+    they describe the average wave of the kernel.
+    """
+    import collections
+    if which == "prefill":
+        key, fname = PREFILL, "kda_prefill_64k_waits.md"
+        title = "KDA prefill (B=1 H=56 T=65536 d=128)"
+        cmd_tail = ("python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --segments 0 --no-configs --no-backward "
+                    "--no-host-cost --no-decode --gate-logits none --no-qknorm")
+        waves, chunks = 224 * 12, 65536 // 16
+        srcs = None
+    else:
+        key, fname = "bwd_chunk_kernel", "kda_bwd_b4_h16_t4096_waits.md"
+        title = "KDA backward chunk kernel (B=4 H=16 T=4096 d=128)"
+        cmd_tail = "python3 bench.py --backward-only --steps 2"
+        waves, chunks = 256 * 8, 4096 // 16
+        srcs = BWD_SOURCES
+    rows = _csv(ds, "counter_collection.csv")
+    per = collections.defaultdict(list)
+    for r in rows:
+        if key in r["Kernel_Name"]:
+            per[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if not per:
+        raise SystemExit("no %s dispatches under %s" % (key, ds))
+    m = {k: statistics.mean(v) for k, v in per.items()}
+    active = m["GRBM_GUI_ACTIVE"] / xcds
+    wave_cyc = 4.0 * m["SQ_WAVE_CYCLES"]
+    share = lambda c, scale: 100.0 * scale * m[c] / wave_cyc
+    cmd = "rocprofv3 --pmc %s --output-format csv -d DIR_S -o waits -- %s" % (WAIT_COUNTERS, cmd_tail)
+    lines = ["# rocprofv3: %s, where the waves' cycles go" % title, "",
+             "Commands (from the repository root):", "", "    " + cmd,
+             "    python3 bench_traffic.py --waits %s DIR_S profiles" % which, "",
+             "Kernel source hash: %s %s" % (which, bench.source_hash(srcs) if srcs else bench.source_hash()), "",
+             "| figure | value |", "|---|---|",
+             "| GPU active cycles per launch (GRBM_GUI_ACTIVE / %d XCDs) | %.4g |" % (xcds, active),
+             "| wave-cycles per launch (4 x SQ_WAVE_CYCLES) | %.4g |" % wave_cyc,
+             "| the same per wave and chunk (%d waves, %d chunks) | %.0f |" % (waves, chunks, wave_cyc / (waves * chunks)),
+             "| waiting on a dependency, count or barrier (4 x SQ_WAIT_ANY) | %.1f%% |" % share("SQ_WAIT_ANY", 4),
+             "| ready, waiting for issue (4 x SQ_WAIT_INST_ANY) | %.1f%% |" % share("SQ_WAIT_INST_ANY", 4),
+             "| issuing (4 x SQ_ACTIVE_INST_ANY) | %.1f%% |" % share("SQ_ACTIVE_INST_ANY", 4),
+             "| of which LDS instructions (4 x SQ_ACTIVE_INST_LDS) | %.1f%% |" % share("SQ_ACTIVE_INST_LDS", 4),
+             "| ready, waiting for LDS issue (4 x SQ_WAIT_INST_LDS) | %.1f%% |" % share("SQ_WAIT_INST_LDS", 4),
+             "| MFMA busy while another vector instruction issued (SQ_VALU_MFMA_COEXEC_CYCLES / (active x %d SIMDs)) | %.1f%% |" % (
+                 1024, 100.0 * m["SQ_VALU_MFMA_COEXEC_CYCLES"] / (active * 1024)),
+             "", "Shares are of the waves' lifetime (wave-cycles), averaged over all waves of the kernel: waiting, "
+             "ready and issuing add up to it. The LDS rows are parts of the issuing and ready rows."]
+    os.makedirs(out, exist_ok=True)
+    with open(os.path.join(out, fname), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
+    if len(sys.argv) == 5 and sys.argv[1] == "--waits" and sys.argv[2] in ("prefill", "backward"):
+        waits(sys.argv[2], sys.argv[3], sys.argv[4])
+        sys.exit(0)
     if len(sys.argv) == 4 and sys.argv[1] == "--backward-util":
         backward_utilisation(sys.argv[2], sys.argv[3])
         sys.exit(0)

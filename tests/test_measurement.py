@@ -77,6 +77,29 @@ def test_counter_scaling_uses_the_copy_before_the_first_kda_kernel(tmp_path):
     assert (sf, sw) == (pytest.approx(2.0), pytest.approx(1.0))
 
 
+def test_wait_shares_are_fractions_of_the_wave_lifetime(tmp_path):
+    # quad-cycle counters: 1000 wave quad-cycles, of which 400 waiting, 350 ready, 250 issuing (100 of them LDS)
+    vals = {"SQ_WAVE_CYCLES": 1000, "SQ_WAIT_ANY": 400, "SQ_WAIT_INST_ANY": 350, "SQ_ACTIVE_INST_ANY": 250,
+            "SQ_ACTIVE_INST_LDS": 100, "SQ_WAIT_INST_LDS": 50, "SQ_VALU_MFMA_COEXEC_CYCLES": 1024 * 10,
+            "GRBM_GUI_ACTIVE": 8 * 100}
+    rows = []
+    for d in ("3", "4"):  # two launches with equal counts; another kernel's counts are ignored
+        for c, v in vals.items():
+            rows.append({"Dispatch_Id": d, "Kernel_Name": PRE, "Counter_Name": c, "Counter_Value": str(v)})
+    rows.append({"Dispatch_Id": "5", "Kernel_Name": COPY, "Counter_Name": "SQ_WAIT_ANY", "Counter_Value": "9e9"})
+    write_csv(str(tmp_path / "s" / "x_counter_collection.csv"), rows)
+    bench_traffic.waits("prefill", str(tmp_path / "s"), str(tmp_path / "out"))
+    text = (tmp_path / "out" / "kda_prefill_64k_waits.md").read_text()
+    for row in ("| wave-cycles per launch (4 x SQ_WAVE_CYCLES) | 4000 |",
+                "| waiting on a dependency, count or barrier (4 x SQ_WAIT_ANY) | 40.0% |",
+                "| ready, waiting for issue (4 x SQ_WAIT_INST_ANY) | 35.0% |",
+                "| issuing (4 x SQ_ACTIVE_INST_ANY) | 25.0% |",
+                "| of which LDS instructions (4 x SQ_ACTIVE_INST_LDS) | 10.0% |",
+                "| GPU active cycles per launch (GRBM_GUI_ACTIVE / 8 XCDs) | 100 |"):
+        assert row in text, row
+    assert "| 10.0% |" in text.split("COEXEC")[1]  # 1024 x 10 co-issue cycles over 100 active cycles x 1024 SIMDs
+
+
 def test_source_hash_tracks_the_kernel_sources():
     # the traffic figures are tied to these files; every prefill source is listed
     names = sorted(os.path.basename(f) for f in bench.KERNEL_SOURCES)
