@@ -214,7 +214,7 @@ def segmented(dt, out, n_seg):
     print("\n".join(lines))
 
 
-BWD_KERNELS = (("prefill_mfma_kernel<true, 0, 0>", "forward with a state checkpoint every 16 tokens"),
+BWD_KERNELS = (("prefill_mfma_kernel<true, 0, 1>", "forward with a state checkpoint every 16 tokens, no o"),
                ("bwd_chunk_kernel", "chunk-form adjoint on fp32 matrix cores, 32-column slices"),
                ("bwd_sum_kernel", "sum of the slices' partial sums (dq, dk, dg, dbeta)"))
 
@@ -251,6 +251,8 @@ def backward(dt, df, dw, out):
              "| kernel | role | calls | avg us | min us | scaled HBM bytes per launch |", "|---|---|---|---|---|---|"]
     total_t, total_b = 0.0, 0.0
     for key, role in BWD_KERNELS:
+        if not any(key in r["Name"] for r in stats):
+            raise SystemExit("kernel %s not in the trace under %s" % (key, dt))
         f, _ = mean_for(fetch, key)
         w, _ = mean_for(write, key)
         hb = (f or 0.0) * 1024 * sf + (w or 0.0) * 1024 * sw
