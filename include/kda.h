@@ -113,6 +113,12 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
  *               checkpoints (the call is then exactly kda_chunk_fwd).
  *   ckpt_every  tokens between checkpoints, a positive multiple of the
  *               16-token chunk; ignored when ckpt is NULL.
+ *   o           as for kda_chunk_fwd, or NULL when ckpt is given: then only
+ *               the checkpoints and hT are written, by a pass that skips the
+ *               output's work (q, its scaled operand and the products that
+ *               form o); the states are bit-identical to those of a call with
+ *               o.  A NULL o without ckpt (and T > 0) is
+ *               KDA_ERR_INVALID_ARGUMENT.
  *
  * All other arguments, the layouts and the errors are those of kda_chunk_fwd;
  * a ckpt_every that is not a positive multiple of 16 is

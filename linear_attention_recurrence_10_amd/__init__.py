@@ -334,13 +334,15 @@ def chunk_fwd_kcp_noalloc(q, k, v, g, beta, h0=None, *, n_seg: int, scale: float
 
 
 def chunk_fwd_ckpt(q, k, v, g, beta, h0=None, *, ckpt_every: int, scale: float | None = None, o=None,
-                   hT=None, ckpt=None, output_final_state: bool = True, stream=None):
+                   hT=None, ckpt=None, output_final_state: bool = True, write_o: bool = True, stream=None):
     """Chunked KDA prefill that also returns state checkpoints (``kda_chunk_fwd_ckpt``).
 
     Arguments as in :func:`chunk_fwd`; ``ckpt_every`` is the number of tokens
     between checkpoints (a positive multiple of 16).  Returns (o, hT, ckpt)
     with ckpt [T // ckpt_every, B, H, Dk, Dv] fp32: ckpt[i] is the state
-    after the first (i + 1) * ckpt_every tokens, usable as ``h0``.
+    after the first (i + 1) * ckpt_every tokens, usable as ``h0``.  With
+    ``write_o=False`` no output is formed (o is None; pass no ``o``): only the
+    states are written, by a cheaper pass.
     """
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, q.dtype)
@@ -350,9 +352,13 @@ def chunk_fwd_ckpt(q, k, v, g, beta, h0=None, *, ckpt_every: int, scale: float |
     Dv = v.shape[-1]
     if h0 is not None:
         _need(h0, "h0", torch.float32)
-    if o is None:
-        o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
-    _need(o, "o", torch.float32)
+    if not write_o:
+        if o is not None:
+            raise ValueError("write_o=False takes no o")
+    else:
+        if o is None:
+            o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
+        _need(o, "o", torch.float32)
     if hT is None and output_final_state:
         hT = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
     if hT is not None:
@@ -362,7 +368,7 @@ def chunk_fwd_ckpt(q, k, v, g, beta, h0=None, *, ckpt_every: int, scale: float |
         ckpt = torch.empty((n_ckpt, B, H, Dk, Dv), dtype=torch.float32, device=q.device)
     _need(ckpt, "ckpt", torch.float32)
     shapes_ok = (k.shape == q.shape and g.shape == q.shape and v.shape[:3] == (B, T, H)
-                 and beta.shape == (B, T, H) and o.shape == (B, T, H, Dv)
+                 and beta.shape == (B, T, H) and (o is None or o.shape == (B, T, H, Dv))
                  and (h0 is None or h0.shape == (B, H, Dk, Dv))
                  and (hT is None or hT.shape == (B, H, Dk, Dv))
                  and ckpt.shape == (n_ckpt, B, H, Dk, Dv))

@@ -143,7 +143,7 @@ kda_status chunk_fwd(const void *q, const void *k, const void *v, const void *g,
                      const float *beta, const float *h0, float *o, float *hT, float *ckpt, int64_t ckpt_every,
                      int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale,
                      void *stream, kda::PrefillArgs *out = nullptr, bool device_checks = true,
-                     float qk_eps = 0.f) {
+                     float qk_eps = 0.f, bool o_optional = false) {
     if (B <= 0 || H <= 0 || Dk <= 0 || Dv <= 0 || T < 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "sizes must be positive (T >= 0): B=%lld T=%lld H=%lld Dk=%lld Dv=%lld",
                     (long long)B, (long long)T, (long long)H, (long long)Dk, (long long)Dv);
@@ -152,8 +152,11 @@ kda_status chunk_fwd(const void *q, const void *k, const void *v, const void *g,
     if (Dk != Dv || (Dk != 16 && Dk != 128))
         return fail(KDA_ERR_UNSUPPORTED, "head dims Dk=%lld Dv=%lld: only Dk == Dv in {16, 128} is built",
                     (long long)Dk, (long long)Dv);
-    if (T > 0 && (!q || !k || !v || !g || !beta || !o))
+    if (T > 0 && (!q || !k || !v || !g || !beta))
         return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and o must be non-null when T > 0");
+    if (T > 0 && !o && !(o_optional && ckpt))
+        return fail(KDA_ERR_INVALID_ARGUMENT, o_optional ? "o may be null only when ckpt is given"
+                                                         : "q, k, v, g, beta and o must be non-null when T > 0");
     if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
     if (ckpt && (ckpt_every <= 0 || ckpt_every % kda::kChunk != 0))
         return fail(KDA_ERR_INVALID_ARGUMENT, "ckpt_every=%lld must be a positive multiple of %d",
@@ -236,7 +239,7 @@ kda_status kda_chunk_fwd_ckpt(const void *q, const void *k, const void *v, const
                               int64_t T, int64_t H, int64_t Dk, int64_t Dv, kda_dtype in_dtype, float scale,
                               void *stream) {
     return chunk_fwd(q, k, v, g, kda::kGateLogDecay, 0.f, beta, h0, o, hT, ckpt, ckpt_every, B, T, H, Dk, Dv,
-                     in_dtype, scale, stream);
+                     in_dtype, scale, stream, nullptr, true, 0.f, /*o_optional=*/true);
 }
 
 kda_status kda_chunk_fwd_gate(const void *q, const void *k, const void *v, const void *x, kda_dtype gate_dtype,

@@ -145,6 +145,20 @@ def test_ckpt_must_not_overlap(lib):
     assert b"ckpt overlaps o" in lib.kda_last_error()
 
 
+def test_ckpt_null_output_needs_checkpoints(lib):
+    ptrs = [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(9)]
+    ptrs[6] = None    # no o, and no checkpoints either: nothing would be written but hT
+    ptrs[8] = None
+    assert chunk_ckpt(lib, ptrs=ptrs) == 1
+    assert b"o may be null only when ckpt is given" in lib.kda_last_error()
+    # with checkpoints the arguments are valid: the call gets as far as the device check
+    ptrs[8] = ctypes.c_void_p(0x1000000 * 9)
+    assert chunk_ckpt(lib, ptrs=ptrs) == 4
+    # the plain entry never takes a null o
+    assert lib.kda_chunk_fwd(*ptrs[:6], None, ptrs[7], 1, 256, 1, 128, 128, 1, 0.0, None) == 1
+    assert b"o must be non-null" in lib.kda_last_error()
+
+
 def test_ckpt_null_ignores_interval(lib):
     ptrs = [P] * 9
     ptrs[8] = None

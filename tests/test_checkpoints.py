@@ -51,6 +51,22 @@ def test_checkpoints_match_oracle_prefix_states(dtype, D, T, every):
     assert rel_err(o.cpu(), o_ref) <= tol and rel_err(hT.cpu(), h_ref) <= tol
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 128), ("f32", 16)])
+@pytest.mark.parametrize("T,every", [(200, 48), (37, 16), (8, 16)])
+def test_states_without_output_are_bit_identical(dtype, D, T, every):
+    # the pass that writes no o (the checkpoint pass of the backward) forms the
+    # same states as the full prefill, to the bit
+    say("case ckpt without o dtype=%s D=%d T=%d every=%d" % (dtype, D, T, every))
+    x = kda_inputs.prefill_inputs(2, T, 3, D, dtype, h0=True, seed=63, device=DEV)
+    _, h1, ck1 = fwd_ckpt(x, every, x["h0"])
+    o2, h2, ck2 = kda.chunk_fwd_ckpt(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], ckpt_every=every,
+                                     write_o=False)
+    torch.cuda.synchronize()
+    assert o2 is None
+    assert ck1.shape == ck2.shape == (T // every, 2, 3, D, D)
+    assert torch.equal(h1, h2) and torch.equal(ck1, ck2)
+
+
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 16)])
 def test_checkpointing_leaves_outputs_unchanged(dtype, D):
     x = kda_inputs.prefill_inputs(1, 320, 4, D, dtype, h0=True, seed=62, device=DEV)
