@@ -16,7 +16,7 @@ import threading
 
 import torch
 
-__all__ = ["chunk_bwd", "bwd_ws_bytes", "chunk_fwd", "chunk_fwd_ckpt", "chunk_fwd_gate", "chunk_fwd_kcp",
+__all__ = ["chunk_bwd", "bwd_ws_bytes", "chunk_fwd", "chunk_fwd_ckpt", "chunk_fwd_gate", "chunk_fwd_kcp", "chunk_kda",
            "chunk_fwd_kcp_noalloc", "chunk_fwd_qknorm", "kcp_ws_bytes", "decode_step", "decode_step_qknorm",
            "KdaError", "library", "library_path", "version"]
 
@@ -437,6 +437,32 @@ def chunk_bwd(q, k, v, g, beta, dO, h0=None, dhT=None, *, scale: float | None = 
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(ws), ws_bytes,
                              B, T, H, Dk, Dv, _dtype_code(q), float(scale or 0.0), _stream(stream)))
     return dq, dk, dv, dg, dbeta, dh0
+
+
+class _ChunkKDA(torch.autograd.Function):
+    """The prefill as an autograd function: forward is kda_chunk_fwd, backward kda_chunk_bwd."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, beta, h0, scale):
+        o, hT = chunk_fwd(q, k, v, g, beta, h0, scale=scale)
+        ctx.save_for_backward(q, k, v, g, beta, h0)
+        ctx.scale = scale
+        return o, hT
+
+    @staticmethod
+    def backward(ctx, dO, dhT):
+        q, k, v, g, beta, h0 = ctx.saved_tensors
+        need_dh0 = h0 is not None and ctx.needs_input_grad[5]
+        dq, dk, dv, dg, dbeta, dh0 = chunk_bwd(q, k, v, g, beta, dO.float().contiguous(), h0,
+                                               dhT.float().contiguous(), scale=ctx.scale, need_dh0=need_dh0)
+        # the gradients of q, k and v take their inputs' dtype (rounded from fp32 for bf16 inputs)
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), dg, dbeta, dh0, None
+
+
+def chunk_kda(q, k, v, g, beta, h0=None, *, scale: float | None = None):
+    """Differentiable chunked KDA prefill: returns (o, hT) as :func:`chunk_fwd`,
+    with gradients for q, k, v, g, beta and h0 from :func:`chunk_bwd`."""
+    return _ChunkKDA.apply(q, k, v, g, beta, h0, scale)
 
 
 def decode_step(q, k, v, g, beta, state, *, scale: float | None = None, o=None, stream=None):

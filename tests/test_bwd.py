@@ -184,3 +184,34 @@ def test_bwd_linear_in_upstream_gradients():
     g3 = run(x, 2.0 * dO1 - 0.5 * dO2, 2.0 * dh1 - 0.5 * dh2)
     for n, a, b, c in zip(NAMES, g1, g2, g3):
         assert rel_err(c.cpu(), (2.0 * a - 0.5 * b).cpu()) < 1e-4, n
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 128), ("f32", 16)])
+def test_autograd_function_matches_chunk_bwd(dtype, D):
+    # chunk_kda: the forward is chunk_fwd and autograd's gradients are
+    # chunk_bwd's for the same upstream gradients, to the bit (cast to the
+    # inputs' dtype for q, k and v)
+    say("case autograd dtype=%s D=%d" % (dtype, D))
+    x = kda_inputs.prefill_inputs(1, 70, 2, D, dtype, h0=True, seed=71, device=DEV)
+    names = ("q", "k", "v", "g", "beta", "h0")
+    leaves = {n: x[n].detach().clone().requires_grad_(True) for n in names}
+    o, hT = kda.chunk_kda(*(leaves[n] for n in names))
+    dO, dhT = upstream(1, 70, 2, D, seed=72)
+    ((o * dO).sum() + (hT * dhT).sum()).backward()
+    torch.cuda.synchronize()
+    o_ref, h_ref = kda.chunk_fwd(*(x[n] for n in names))
+    ref = run(x, dO, dhT)
+    assert torch.equal(o.detach(), o_ref) and torch.equal(hT.detach(), h_ref)
+    for n, r in zip(names, ref):
+        got = leaves[n].grad
+        assert got.dtype == x[n].dtype, n
+        assert torch.equal(got, r.to(x[n].dtype)), n
+    # without an initial state there is no h0 gradient, and an unused output gives a zero upstream gradient
+    leaves2 = {n: x[n].detach().clone().requires_grad_(True) for n in names[:5]}
+    o2, _ = kda.chunk_kda(*(leaves2[n] for n in names[:5]))
+    (o2 * dO).sum().backward()
+    torch.cuda.synchronize()
+    ref2 = kda.chunk_bwd(*(x[n] for n in names[:5]), dO, None, None, need_dh0=False)
+    torch.cuda.synchronize()
+    for n, r in zip(names[:5], ref2[:5]):
+        assert torch.equal(leaves2[n].grad, r.to(x[n].dtype)), n
