@@ -9,7 +9,9 @@ on it:
   may then not all be resident) matches the oracle;
 * two launches running at the same time on two streams (their epochs interleave
   in the same report slots) give bitwise the results of separate launches;
-* with enough heads to fill the report array's range, the results are right.
+* with enough heads to fill the report array's range, the results are right;
+* past that range (more than 16384 heads) the launch runs unpaced and the
+  results are right.
 """
 from __future__ import annotations
 
@@ -78,3 +80,18 @@ def test_many_heads_across_the_report_range():
     o_ref, s_ref = oracle_sampled(x, heads, cols)
     assert rel_err(pick(o, heads, cols), o_ref) <= tol_for("bf16")
     assert rel_err(pick(hT, heads, cols, head_dim=1, col_dim=3), s_ref) <= tol_for("bf16")
+
+
+def test_more_heads_than_report_slots_runs_unpaced():
+    # B H = 16400 heads (past the 16384 the report array serves): no slice
+    # reports or waits, and the results are right; a ragged 20-token sequence
+    say("case unpaced: B=2 H=8200 T=20")
+    x = kda_inputs.prefill_inputs(2, 20, 8200, 128, "bf16", h0=True, seed=95, device=DEV)
+    o, hT = fwd(x)
+    torch.cuda.synchronize()
+    heads, cols = [0, 4099, 8199], [0, 77, 127]
+    o_ref, s_ref = oracle_sampled(x, heads, cols)
+    eo = rel_err(pick(o, heads, cols), o_ref)
+    eh = rel_err(pick(hT, heads, cols, head_dim=1, col_dim=3), s_ref)
+    say("  16400 heads: o %.3e hT %.3e" % (eo, eh))
+    assert eo <= tol_for("bf16") and eh <= tol_for("bf16")
