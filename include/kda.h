@@ -1,5 +1,6 @@
 /*
- * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library: the
+ * chunked prefill, the decode step and the prefill's backward pass.
  *
  * The operation (per batch row b and head h; one state per head):
  *
@@ -38,8 +39,10 @@
  *  - g is the log-decay, expected in [-5, 0] (the bounded gate above); values
  *    outside are not clamped, but g < -5 may underflow the in-chunk factors.
  *  - scale <= 0 selects Dk^-1/2.
- *  - Supported shapes: Dk == Dv in {16, 128}.  Indices are 64-bit, so any B*T*H
- *    that fits in device memory is accepted.
+ *  - Supported shapes: Dk == Dv in {16, 128}.  Indices are 64-bit, so T and
+ *    B*T*H are limited by device memory only; a prefill with B*H above
+ *    2^25 - 1 (B*n_seg*H for the segmented one) or a decode step with B*H
+ *    above 2^31 - 1 exceeds one launch's grid and is KDA_ERR_UNSUPPORTED.
  *  - Argument errors are detected before anything is launched and return
  *    KDA_ERR_INVALID_ARGUMENT or KDA_ERR_UNSUPPORTED; kda_last_error() then
  *    describes the problem.  A failed launch returns KDA_ERR_LAUNCH.  No C++
@@ -285,9 +288,8 @@ uint64_t kda_chunk_fwd_kcp_noalloc_max_bytes(void);
  *          forward state after every 16 tokens (written here by the prefill
  *          kernels) and per-slice partial sums.
  *
- * The outputs must not overlap each other, the inputs or ws.  dq is also used
- * as scratch for the forward pass's o before the gradient is written there.
- * Results are deterministic (fixed summation order).  All other rules, the
+ * The outputs must not overlap each other, the inputs or ws.  Results are
+ * deterministic (fixed summation order).  All other rules, the
  * layouts and the errors are those of kda_chunk_fwd; T == 0 writes dh0 = dhT
  * (or zeros).
  *
