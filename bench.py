@@ -283,7 +283,34 @@ def decode_host_cost(kda, torch, calls=200):
     t1 = time.perf_counter()
     torch.cuda.synchronize()
     assert st == 0
-    return {"batch": "B=1 H=8 d=128 bf16", "calls": calls, "host_us_per_call": 1e6 * (t1 - t0) / calls}
+    out = {"batch": "B=1 H=8 d=128 bf16", "calls": calls, "host_us_per_call": 1e6 * (t1 - t0) / calls}
+    # wall time per step to completion: an eager loop of calls, and the same
+    # steps replayed from a captured HIP graph of 32 steps (no host work per step)
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        lib.kda_decode_step(*args)
+    torch.cuda.synchronize()
+    out["eager_us_per_step"] = 1e6 * (time.perf_counter() - t0) / calls
+    steps = 32
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            gargs = args[:-1] + [cs]
+            for _ in range(steps):
+                lib.kda_decode_step(*gargs)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, calls // steps)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        out["graph_us_per_step"] = 1e6 * (time.perf_counter() - t0) / (reps * steps)
+    except RuntimeError as e:  # reported, not fatal: the figure is context for serving loops
+        out["graph_us_per_step"] = None
+        out["graph_error"] = str(e)[:200]
+    return out
 
 
 def cpu_model():
